@@ -1,0 +1,16 @@
+"""CPU oracle for the W8A8 linear layer -- test infrastructure only.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package. It shares nothing with the HIP library.
+"""
+from .oracle import (  # noqa: F401
+    build_oracle,
+    bf16_rne_from_f64,
+    bsr_gemm_i32,
+    epilogue_bf16,
+    gemm_i32,
+    load_oracle,
+    num_threads,
+    quantize_rows_bf16,
+    quantize_rows_f32,
+)

@@ -1,0 +1,147 @@
+"""ctypes front end of the C oracle (w8a8_oracle.c) -- test infrastructure only.
+
+Arrays are numpy: bf16 values travel as their uint16 bit patterns. Every
+function here only marshals arguments; the arithmetic is in the C file, whose
+header states the passages each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "w8a8_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+# IEEE semantics are part of the definition: no contraction, no fast-math.
+CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+          "-Wall", "-Wextra", "-Werror"]
+
+
+def build_oracle() -> str:
+    """Compile the oracle with gcc into oracle/liboracle.so (always rebuilds)."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_oracle():
+    """Load liboracle.so, building it first only if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build_oracle()
+    lib = ctypes.CDLL(_LIB)
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.oracle_quantize_rows_bf16.argtypes = [p, i64, i64, p, p]
+    lib.oracle_quantize_rows_bf16.restype = None
+    lib.oracle_quantize_rows_f32.argtypes = [p, i64, i64, p, p]
+    lib.oracle_quantize_rows_f32.restype = None
+    lib.oracle_gemm_i32.argtypes = [p, p, i64, i64, i64, p]
+    lib.oracle_gemm_i32.restype = ctypes.c_int
+    lib.oracle_bf16_rne_from_f64.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_rne_from_f64.restype = ctypes.c_uint16
+    lib.oracle_epilogue_bf16.argtypes = [p, p, p, i64, i64, p]
+    lib.oracle_epilogue_bf16.restype = None
+    lib.oracle_bsr_gemm_i32.argtypes = [p, i64, i64, p, p, p, i64, i64, p]
+    lib.oracle_bsr_gemm_i32.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.dtype(dtype):
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def quantize_rows_bf16(x_bits: np.ndarray):
+    """X bf16 [M,K] (uint16 bit patterns) -> (q int8 [M,K], s float32 [M])."""
+    x = _c(x_bits, np.uint16)
+    M, K = x.shape
+    q = np.empty((M, K), np.int8)
+    s = np.empty((M,), np.float32)
+    load_oracle().oracle_quantize_rows_bf16(_ptr(x), M, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quantize_rows_f32(x: np.ndarray):
+    """W fp32 [N,K] -> (q int8 [N,K], s float32 [N]), one scale per row."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    q = np.empty((M, K), np.int8)
+    s = np.empty((M,), np.float32)
+    load_oracle().oracle_quantize_rows_f32(_ptr(x), M, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def gemm_i32(xq: np.ndarray, wq: np.ndarray) -> np.ndarray:
+    """acc int32 [M,N] = xq [M,K] . wq [N,K]^T, exact; raises if it leaves int32."""
+    xq = _c(xq, np.int8)
+    wq = _c(wq, np.int8)
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K != K2:
+        raise ValueError("K mismatch")
+    acc = np.empty((M, N), np.int32)
+    rc = load_oracle().oracle_gemm_i32(_ptr(xq), _ptr(wq), M, N, K, _ptr(acc))
+    if rc != 0:
+        raise OverflowError("int8 dot product leaves the int32 range")
+    return acc
+
+
+def bf16_rne_from_f64(v: float) -> int:
+    """Bit pattern of the bf16 nearest to v (ties to even)."""
+    return int(load_oracle().oracle_bf16_rne_from_f64(float(v)))
+
+
+def epilogue_bf16(acc: np.ndarray, sx: np.ndarray, sw: np.ndarray) -> np.ndarray:
+    """out bf16 bits [M,N] = bf16_rne(acc * sx[m] * sw[n]) evaluated in float64."""
+    acc = _c(acc, np.int32)
+    sx = _c(sx, np.float32)
+    sw = _c(sw, np.float32)
+    M, N = acc.shape
+    if sx.shape != (M,) or sw.shape != (N,):
+        raise ValueError("scale shapes")
+    out = np.empty((M, N), np.uint16)
+    load_oracle().oracle_epilogue_bf16(_ptr(acc), _ptr(sx), _ptr(sw), M, N, _ptr(out))
+    return out
+
+
+def bsr_gemm_i32(xq: np.ndarray, crow: np.ndarray, col: np.ndarray, values: np.ndarray,
+                 N: int) -> np.ndarray:
+    """acc int32 [M,N] over the stored blocks of a BSR weight (values [nnzb,bs,bs])."""
+    xq = _c(xq, np.int8)
+    crow = _c(crow, np.int32)
+    col = _c(col, np.int32)
+    values = _c(values, np.int8)
+    M, K = xq.shape
+    bs = values.shape[1] if values.ndim == 3 else 64
+    if values.ndim != 3 or values.shape[2] != bs or N % bs or K % bs:
+        raise ValueError("BSR shapes")
+    if crow.shape != (N // bs + 1,) or col.shape[0] != values.shape[0]:
+        raise ValueError("BSR index shapes")
+    acc = np.empty((M, N), np.int32)
+    rc = load_oracle().oracle_bsr_gemm_i32(_ptr(xq), M, K, _ptr(crow), _ptr(col),
+                                           _ptr(values), bs, N, _ptr(acc))
+    if rc != 0:
+        raise OverflowError("int8 dot product leaves the int32 range")
+    return acc
+
+
+def num_threads() -> int:
+    return int(load_oracle().oracle_num_threads())

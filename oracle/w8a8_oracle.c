@@ -1,0 +1,193 @@
+/*
+ * CPU oracle for the dynamically quantized int8 linear layer (W8A8).
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the plain, slow, obviously correct
+ * definition that the GPU path is checked against. It shares no code, header,
+ * table or helper with the HIP library; only the test suite, the smoke check
+ * and the benchmark's CPU-baseline leg may load it. The product path never
+ * calls it.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (never -ffast-math,
+ * so IEEE-754 binary32 division, round-to-nearest-even and subnormals hold).
+ *
+ * What it computes, with the passages it follows:
+ *
+ *   quantize (per row of X, per output channel of W):
+ *     absmax = max_k |x[k]|            -- "int8 dynamicquant", pytorch/ao PR #821;
+ *                                         absmax search in the Paddle
+ *                                         sparse_fc PR #41770, spmm_plugin.cu
+ *                                         weight-scale hunk
+ *     s      = fl32(absmax / 127)      -- same hunk: the scale is the float
+ *                                         quotient of the absmax by 127
+ *     q[k]   = clamp(rint(fl32(x[k] / s)), -127, 127)
+ *                                      -- clamp before the integer cast, vLLM
+ *                                         csrc/quantization log (FP8 clamp
+ *                                         commit); half-to-even rounding
+ *     absmax == 0  =>  s = 0 and q = 0 (the pages are silent; plainest reading)
+ *
+ *   int8 GEMM:   acc[m,n] = sum_k xq[m,k] * wq[n,k] as an exact integer,
+ *                which must fit int32 -- "triton dot accumulator uses int32",
+ *                pytorch/ao PR #821; the 2**31 / 2**14 headroom remark in the
+ *                same thread bounds K.
+ *   epilogue:    out[m,n] = bf16_rne(acc * sx[m] * sw[n]) in float64, rounded
+ *                once from float64 to bf16 -- "i8i8 -> bf16 matmul to
+ *                maintain accuracy", pytorch/ao PR #821, Changes list.
+ *   BSR:         the same sum taken only over the stored 64x64 blocks
+ *                (crow_indices / col_indices / values), pytorch/ao PR #821
+ *                custom-op paragraph and the bsr_dense_addmm warning (Ms=64,
+ *                Ks=64, beta=0, alpha=1).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* bf16 is the top half of a binary32: widening is exact. */
+static float bf16_bits_to_float(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* One row of the absmax/127 rule, on values already widened to float. */
+static void quantize_one_row(const float *x, int64_t K, int8_t *q, float *s_out) {
+    float absmax = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        float a = fabsf(x[k]);
+        if (a > absmax) absmax = a;
+    }
+    float s = absmax / 127.0f; /* one correctly rounded binary32 division */
+    *s_out = s;
+    for (int64_t k = 0; k < K; ++k) {
+        if (s == 0.0f) {
+            q[k] = 0;
+            continue;
+        }
+        float t = x[k] / s;  /* correctly rounded binary32 quotient */
+        float r = rintf(t);  /* half to even (default rounding mode) */
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        q[k] = (int8_t)r;
+    }
+}
+
+/* X bf16 [M,K] row-major (raw bit patterns) -> q int8 [M,K], s fp32 [M]. */
+void oracle_quantize_rows_bf16(const uint16_t *x, int64_t M, int64_t K, int8_t *q, float *s) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float *row = (float *)malloc((size_t)(K > 0 ? K : 1) * sizeof(float));
+        for (int64_t k = 0; k < K; ++k) row[k] = bf16_bits_to_float(x[m * K + k]);
+        quantize_one_row(row, K, q + m * K, s + m);
+        free(row);
+    }
+}
+
+/* W fp32 [N,K] row-major -> q int8 [N,K], s fp32 [N] (per output channel). */
+void oracle_quantize_rows_f32(const float *x, int64_t M, int64_t K, int8_t *q, float *s) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) quantize_one_row(x + m * K, K, q + m * K, s + m);
+}
+
+/*
+ * acc[m,n] = sum_k xq[m,k] * wq[n,k], summed exactly in int64.
+ * Returns 0, or -1 if any sum falls outside int32 (acc then holds garbage).
+ */
+int oracle_gemm_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
+                    int32_t *acc) {
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t sum = 0;
+            for (int64_t k = 0; k < K; ++k) sum += (int64_t)xq[m * K + k] * (int64_t)wq[n * K + k];
+            if (sum > INT32_MAX || sum < INT32_MIN) bad = 1;
+            acc[m * N + n] = (int32_t)sum;
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Round a float64 to the nearest bf16 (8 significant bits, binary32 exponent
+ * range, subnormals kept), ties to even; returns the bf16 bit pattern.
+ * v = n * quantum with quantum a power of two, so n is exact in float64 and
+ * rounding n to an integer rounds v onto the bf16 grid.
+ */
+uint16_t oracle_bf16_rne_from_f64(double v) {
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80);
+    int e;
+    (void)frexp(a, &e);          /* a in [2^(e-1), 2^e) */
+    int unbiased = e - 1;
+    if (unbiased < -126) unbiased = -126; /* subnormal range: fixed quantum */
+    double quantum = ldexp(1.0, unbiased - 7);
+    double n = a / quantum;      /* exact: division by a power of two */
+    double r = nearbyint(n);     /* half to even */
+    double rounded = r * quantum;
+    if (rounded >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80); /* overflow */
+    float f = (float)rounded;    /* exact: rounded is on the bf16 grid */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (uint16_t)((u >> 16) & 0x7FFF));
+}
+
+/* out[m,n] = bf16_rne(acc[m,n] * sx[m] * sw[n]); sx*sw is exact in float64. */
+void oracle_epilogue_bf16(const int32_t *acc, const float *sx, const float *sw, int64_t M,
+                          int64_t N, uint16_t *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double scale = (double)sx[m] * (double)sw[n];
+            double v = (double)acc[m * N + n] * scale;
+            out[m * N + n] = oracle_bf16_rne_from_f64(v);
+        }
+    }
+}
+
+/*
+ * Block-sparse weight, 'bs' x 'bs' blocks: block j covers output channels
+ * [r*bs, r*bs+bs) for the block row r with crow[r] <= j < crow[r+1] and input
+ * channels [col[j]*bs, col[j]*bs+bs); values[j][i][c] is W[r*bs+i, col[j]*bs+c].
+ * acc[m,n] = sum over the stored blocks of block row n/bs of the int8 products;
+ * channels of block rows with no stored block get 0.
+ * Returns 0, or -1 if any sum falls outside int32.
+ */
+int oracle_bsr_gemm_i32(const int8_t *xq, int64_t M, int64_t K, const int32_t *crow,
+                        const int32_t *col, const int8_t *values, int64_t bs, int64_t N,
+                        int32_t *acc) {
+    int64_t block_rows = N / bs;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t r = 0; r < block_rows; ++r) {
+            for (int64_t i = 0; i < bs; ++i) {
+                int64_t sum = 0;
+                for (int64_t j = crow[r]; j < crow[r + 1]; ++j) {
+                    const int8_t *blk = values + j * bs * bs;
+                    int64_t k0 = (int64_t)col[j] * bs;
+                    for (int64_t c = 0; c < bs; ++c)
+                        sum += (int64_t)xq[m * K + k0 + c] * (int64_t)blk[i * bs + c];
+                }
+                if (sum > INT32_MAX || sum < INT32_MIN) bad = 1;
+                acc[m * N + r * bs + i] = (int32_t)sum;
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* Threads the OpenMP loops above run on (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,295 @@
+"""Pins of the CPU oracle to facts outside itself (no GPU needed).
+
+Each test checks the oracle against something it cannot agree with by
+construction: hand-worked values, exact rational arithmetic, a library routine
+(numpy int64 matmul, PyTorch's float32 -> bf16 cast), a closed-form bound or a
+mathematical invariant.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from exact import bf16 as exact_bf16
+from exact import quantize_row as exact_quantize_row
+from quantized_gemm_quantize_amd.inputs import (bf16_bits_to_f32, bsr_from_dense, dense_from_bsr,
+                                                f32_to_bf16_bits, make_inputs, make_linear)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bits_to_float(b):
+    return float(bf16_bits_to_f32(np.array([b], np.uint16))[0])
+
+
+# --- hand-worked example ---------------------------------------------------
+
+def test_worked_example_2x3(oracle):
+    g = _load("worked_2x3.json")
+    x_bits = f32_to_bf16_bits(np.array(g["x"], np.float32))
+    assert np.array_equal(bf16_bits_to_f32(x_bits), np.array(g["x"], np.float32))  # exact in bf16
+    xq, sx = oracle.quantize_rows_bf16(x_bits)
+    assert sx.tolist() == g["x_scale"]
+    assert xq.tolist() == g["xq"]
+    wq, sw = oracle.quantize_rows_f32(np.array(g["w"], np.float32))
+    assert sw.tolist() == g["w_scale"]
+    assert wq.tolist() == g["wq"]
+    acc = oracle.gemm_i32(xq, wq)
+    assert acc.tolist() == g["acc"]
+    out = oracle.epilogue_bf16(acc, sx, sw)
+    assert bf16_bits_to_f32(out).tolist() == g["out_bf16"]
+    # the exact product, rounded by hand-written rational bf16 rounding
+    for m in range(2):
+        for n in range(2):
+            v = Fraction(g["out_exact"][m][n])
+            assert v == acc[m, n] * Fraction(float(sx[m])) * Fraction(float(sw[n]))
+            assert float(exact_bf16(v)) == g["out_bf16"][m][n]
+
+
+def test_near_ties_divide_by_stored_fp32_scale(oracle):
+    g = _load("near_ties.json")
+    for case in g["cases"]:
+        row = np.array([[case["absmax"], case["x"]]], np.float32)
+        bits = f32_to_bf16_bits(row)
+        assert np.array_equal(bf16_bits_to_f32(bits), row)
+        q, s = oracle.quantize_rows_bf16(bits)
+        assert int(q[0, 0]) == 127
+        assert int(q[0, 1]) == case["q"], case
+        # the same cases through the fp32 entry (weights)
+        q2, s2 = oracle.quantize_rows_f32(row)
+        assert int(q2[0, 1]) == case["q"] and s2[0] == s[0]
+
+
+# --- exact rational reference on small rows --------------------------------
+
+def _special_rows():
+    rows = [
+        np.zeros(16, np.float32),                                    # all-zero row
+        np.full(16, -3.0, np.float32),                               # constant
+        np.array([2.0 ** -130, -2.0 ** -131] + [0.0] * 14, np.float32),   # bf16 subnormals
+        np.array([1e-38, 5e-39, -2e-39] + [1e-40] * 13, np.float32),      # tiny normals/subnormals
+        np.array([3e38, -1.0, 1e30] + [0.5] * 13, np.float32),       # near the top of the range
+        np.array([127.0, 63.5, -0.5, 1.5, 2.5, -2.5, 0.0, -0.0] * 2, np.float32),
+    ]
+    return rows
+
+
+def test_quantize_matches_exact_rationals(oracle):
+    rng = np.random.default_rng(123)
+    rows = _special_rows()
+    for _ in range(60):
+        scale = float(2.0 ** rng.integers(-140, 120))
+        rows.append((rng.standard_normal(16) * scale).astype(np.float32))
+    for _ in range(40):   # heavy-tailed rows with outliers
+        r = rng.standard_normal(16).astype(np.float32)
+        r[rng.integers(0, 16)] *= 40
+        rows.append(r)
+    x = np.stack(rows)
+    bits = f32_to_bf16_bits(x)
+    xb = bf16_bits_to_f32(bits)
+    q, s = oracle.quantize_rows_bf16(bits)
+    for m in range(x.shape[0]):
+        es, eq = exact_quantize_row([Fraction(float(v)) for v in xb[m]])
+        assert Fraction(float(s[m])) == es, m
+        assert q[m].tolist() == eq, m
+    # fp32 entry on rows that are not bf16-representable
+    xf = x + np.float32(1e-3) * rng.standard_normal(x.shape).astype(np.float32)
+    qf, sf = oracle.quantize_rows_f32(xf)
+    for m in range(xf.shape[0]):
+        es, eq = exact_quantize_row([Fraction(float(v)) for v in xf[m]])
+        assert Fraction(float(sf[m])) == es and qf[m].tolist() == eq, m
+
+
+def test_zero_and_subnormal_rows(oracle):
+    x = np.zeros((2, 32), np.float32)
+    x[1, 3] = 2.0 ** -133          # smallest bf16 subnormal
+    x[1, 7] = -(2.0 ** -134) * 3   # not bf16: rounds to -2^-132
+    bits = f32_to_bf16_bits(x)
+    q, s = oracle.quantize_rows_bf16(bits)
+    assert s[0] == 0.0 and not q[0].any()
+    assert s[1] > 0.0                    # subnormal scale, not flushed
+    assert q[1, 7] == -127 and q[1, 3] == 64   # s = 1032 * 2^-149; 2^-133 / s = 63.504 -> 64
+    acc = oracle.gemm_i32(q, np.ones((4, 32), np.int8))
+    out = oracle.epilogue_bf16(acc, s, np.ones(4, np.float32))
+    assert (out[0] == 0).all()           # +0, not -0
+
+
+# --- invariants at workload sizes ------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "prefill_outliers"])
+def test_quantize_invariants(oracle, name):
+    inp = make_inputs(name, M=256 if name != "tiny" else None)
+    q, s = oracle.quantize_rows_bf16(inp.x_bits)
+    x = bf16_bits_to_f32(inp.x_bits).astype(np.float64)
+    s64 = s.astype(np.float64)[:, None]
+    err = np.abs(x - q.astype(np.float64) * s64)
+    assert (err <= s64 * (0.5 + 2.0 ** -16)).all()
+    assert (np.abs(q.astype(np.int32)) <= 127).all()
+    assert (np.abs(q.astype(np.int32)).max(axis=1) == 127).all()
+    # scale equals absmax/127 to within half an fp32 ulp (correct rounding)
+    absmax = np.abs(x).max(axis=1)
+    rel = np.abs(s.astype(np.float64) - absmax / 127.0) / (absmax / 127.0)
+    assert (rel <= 2.0 ** -24).all()
+    wq, sw = oracle.quantize_rows_f32(inp.w)
+    errw = np.abs(inp.w.astype(np.float64) - wq.astype(np.float64) * sw.astype(np.float64)[:, None])
+    assert (errw <= sw.astype(np.float64)[:, None] * (0.5 + 2.0 ** -16)).all()
+
+
+# --- integer GEMM -----------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (2, 3, 5), (5, 8, 3), (8, 8, 8), (3, 1, 64), (17, 33, 48)])
+def test_gemm_equals_numpy_int64(oracle, M, N, K):
+    rng = np.random.default_rng(M * 100 + N * 10 + K)
+    xq = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    wq = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    acc = oracle.gemm_i32(xq, wq)
+    ref = xq.astype(np.int64) @ wq.astype(np.int64).T
+    assert np.array_equal(acc.astype(np.int64), ref)
+    # brute force, element by element, for the tiniest shapes
+    if M * N * K <= 512:
+        for m in range(M):
+            for n in range(N):
+                assert acc[m, n] == sum(int(xq[m, k]) * int(wq[n, k]) for k in range(K))
+
+
+def test_int32_headroom_bound(oracle):
+    # 127*127*K stays below 2^31 up to K = 133144; the largest multiple of 16 is 133136
+    K = 133136
+    ones = np.full((1, K), 127, np.int8)
+    acc = oracle.gemm_i32(ones, ones)
+    assert int(acc[0, 0]) == 127 * 127 * K and 127 * 127 * K < 2 ** 31
+    K2 = 133152
+    big = np.full((1, K2), 127, np.int8)
+    with pytest.raises(OverflowError):
+        oracle.gemm_i32(big, big)
+    neg = np.full((1, K2), -127, np.int8)
+    with pytest.raises(OverflowError):
+        oracle.gemm_i32(big, neg)
+
+
+# --- bf16 rounding and the epilogue ----------------------------------------
+
+def test_bf16_rounding_matches_torch_cast(oracle):
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32)
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    ref = f32_to_bf16_bits(vals)
+    got = np.array([oracle.bf16_rne_from_f64(float(v)) for v in vals], np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_rounding_ties_and_edges(oracle):
+    r = oracle.bf16_rne_from_f64
+    assert r(1.0 + 2.0 ** -8) == 0x3F80               # tie -> even (down)
+    assert r(1.0 + 3 * 2.0 ** -8) == 0x3F82           # tie -> even (up)
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81  # just above the tie
+    assert r(-(1.0 + 2.0 ** -8)) == 0xBF80
+    assert r(2.0 ** -134) == 0x0000                   # subnormal tie -> 0
+    assert r(3 * 2.0 ** -134) == 0x0002               # subnormal tie -> even
+    assert r(2.0 ** -133) == 0x0001
+    assert r(2.0 ** 128 - 2.0 ** 119) == 0x7F80       # rounds up to infinity
+    assert r(2.0 ** 128 - 2.0 ** 119 - 2.0 ** 100) == 0x7F7F
+    assert r(0.0) == 0x0000 and r(-0.0) == 0x8000
+
+
+def test_epilogue_matches_exact_rationals(oracle):
+    rng = np.random.default_rng(11)
+    acc = rng.integers(-2 ** 31, 2 ** 31, (40, 50), dtype=np.int64).astype(np.int32)
+    acc[0, :5] = [0, 1, -1, 2 ** 24 + 1, -(2 ** 31)]
+    sx = (np.abs(rng.standard_normal(40)) * 2.0 ** rng.integers(-30, 10, 40)).astype(np.float32)
+    sw = (np.abs(rng.standard_normal(50)) * 2.0 ** rng.integers(-30, 10, 50)).astype(np.float32)
+    out = oracle.epilogue_bf16(acc, sx, sw)
+    for m in range(40):
+        for n in range(50):
+            exact = int(acc[m, n]) * Fraction(float(sx[m])) * Fraction(float(sw[n]))
+            assert _bits_to_float(out[m, n]) == float(exact_bf16(exact)), (m, n)
+
+
+def test_dequantized_product_error_bound(oracle):
+    """|out - X W^T| is bounded by the quantization errors of X and W plus bf16 rounding."""
+    inp = make_linear(24, 40, 96, seed=5)
+    xq, sx = oracle.quantize_rows_bf16(inp.x_bits)
+    wq, sw = oracle.quantize_rows_f32(inp.w)
+    out = bf16_bits_to_f32(oracle.epilogue_bf16(oracle.gemm_i32(xq, wq), sx, sw)).astype(np.float64)
+    x = bf16_bits_to_f32(inp.x_bits).astype(np.float64)
+    w = inp.w.astype(np.float64)
+    xh = xq.astype(np.float64) * sx.astype(np.float64)[:, None]
+    wh = wq.astype(np.float64) * sw.astype(np.float64)[:, None]
+    bound = np.abs(x - xh) @ np.abs(w).T + np.abs(xh) @ np.abs(w - wh).T
+    exact_q = xh @ wh.T
+    assert (np.abs(exact_q - x @ w.T) <= bound * (1 + 1e-12) + 1e-300).all()
+    assert (np.abs(out - exact_q) <= np.abs(exact_q) * 2.0 ** -8 + 1e-300).all()
+    # a transposed or mis-scaled product would break the bound
+    assert not (np.abs(exact_q.T[:24, :24] - (x @ w.T)[:24, :24]) <= bound[:24, :24]).all()
+
+
+def test_small_outputs_survive_bf16(oracle):
+    """acc * scale far below 1 keeps its value in bf16 (an int8/int32 output flushes it to 0)."""
+    acc = np.array([[3, -5, 1]], np.int32)
+    sx = np.array([1e-4], np.float32)
+    sw = np.array([1e-3, 1e-3, 1e-3], np.float32)
+    out = bf16_bits_to_f32(oracle.epilogue_bf16(acc, sx, sw))
+    assert (out != 0).all()
+    assert np.allclose(out, acc[0] * 1e-7, rtol=2 ** -8)
+    assert (np.rint(acc[0] * 1e-7) == 0).all()
+
+
+# --- block-sparse weight ----------------------------------------------------
+
+def test_bsr_equals_dense_on_densified_weight(oracle):
+    inp = make_linear(40, 256, 192, seed=9, bs=64, zero_frac=0.6)
+    xq, sx = oracle.quantize_rows_bf16(inp.x_bits)
+    wq, sw = oracle.quantize_rows_f32(inp.w)
+    crow, col, values = bsr_from_dense(wq, inp.block_mask, 64)
+    assert np.array_equal(dense_from_bsr(crow, col, values, 256, 192), wq * 0 + np.where(
+        np.repeat(np.repeat(inp.block_mask, 64, 0), 64, 1), wq, 0))
+    acc_bsr = oracle.bsr_gemm_i32(xq, crow, col, values, 256)
+    acc_dense = oracle.gemm_i32(xq, dense_from_bsr(crow, col, values, 256, 192))
+    assert np.array_equal(acc_bsr, acc_dense)
+    assert np.array_equal(acc_bsr.astype(np.int64),
+                          xq.astype(np.int64) @ dense_from_bsr(crow, col, values, 256, 192).astype(np.int64).T)
+
+
+def test_bsr_empty_rows_and_empty_matrix(oracle):
+    rng = np.random.default_rng(2)
+    xq = rng.integers(-127, 128, (8, 128), dtype=np.int8)
+    mask = np.array([[False, False], [True, False], [False, False]])
+    w = rng.integers(-127, 128, (192, 128), dtype=np.int8)
+    crow, col, values = bsr_from_dense(w, mask, 64)
+    assert crow.tolist() == [0, 0, 1, 1] and col.tolist() == [0]
+    acc = oracle.bsr_gemm_i32(xq, crow, col, values, 192)
+    assert not acc[:, :64].any() and not acc[:, 128:].any()
+    assert np.array_equal(acc[:, 64:128].astype(np.int64),
+                          xq[:, :64].astype(np.int64) @ w[64:128, :64].astype(np.int64).T)
+    crow0 = np.zeros(4, np.int32)
+    acc0 = oracle.bsr_gemm_i32(xq, crow0, np.zeros(0, np.int32), np.zeros((0, 64, 64), np.int8), 192)
+    assert not acc0.any()
+
+
+def test_bsr_workload_structure():
+    inp = make_inputs("bsr", M=64)
+    assert inp.block_mask.shape == (80, 20)
+    assert int(inp.block_mask.sum()) == 160
+    nz_blocks = np.abs(inp.w).reshape(80, 64, 20, 64).sum(axis=(1, 3)) > 0
+    assert np.array_equal(nz_blocks, inp.block_mask)
+
+
+def test_prefill_outlier_channels():
+    inp = make_inputs("prefill_outliers", M=64)
+    chans = inp.meta["outlier_channels"]
+    assert len(chans) == 41
+    x = bf16_bits_to_f32(inp.x_bits)
+    ratio = np.abs(x[:, chans]).mean() / np.abs(np.delete(x, chans, axis=1)).mean()
+    assert 15 < ratio < 25
+    # seeded: the same draw twice
+    assert np.array_equal(make_inputs("prefill_outliers", M=64).x_bits, inp.x_bits)
+    assert torch.bfloat16 is not None
