@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the dynamically quantized int8 linear layer on one MI355X.
+
+One step = one pass of the whole layer over one batch of synthetic input:
+w8a8_quantize_rows (per-row absmax/127 int8 quantization of X) followed by
+w8a8_gemm (int8 MFMA GEMM with the fused dequant -> bf16 epilogue), on the
+M=2048, K=N=4096 workload with 1% outlier channels. `value` is the effective
+int8 rate of the step, 2*M*N*K / step time.
+
+The line also carries:
+  roofline     the GEMM kernel alone (the dominant kernel): algorithmic int8
+               ops per launch / average launch time, against the int8 dense
+               MFMA peak; traffic from the committed rocprofv3 PMC record when
+               it was taken on the current kernel source, else null;
+  cpu_baseline the CPU oracle timed on this host on a bounded sample;
+  decode_m16   the M=16 weight-streaming path (K=N=4096): GB/s of the GEMM
+               kernel against HBM peak, with rotated weight copies so the
+               256 MB Infinity Cache cannot serve them.
+
+Inputs are resident in HBM before the timed region; input sets are rotated
+(copies at distinct addresses, more than twice the Infinity Cache in total).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective int8 TOPS (+% of MFMA peak) at M=2048,K=N=4096; GB/s at M=16"
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, TOP/s
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
+MALL_BYTES = 256 << 20      # Infinity Cache
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_tiled_prefill_traffic.json")
+GEMM_SOURCES = ["gemm_tiled.hip", "common.hpp"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="prefill_outliers",
+                    choices=["tiny", "decode", "prefill_outliers", "large_m", "bsr"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+def source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "quantized_gemm_quantize_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def rotation(bytes_per_set: int) -> int:
+    """Copies needed for the rotated sets to exceed twice the Infinity Cache."""
+    return max(2, -(-2 * MALL_BYTES // max(bytes_per_set, 1)) + 1)
+
+
+def time_loop(fn, n: int, torch) -> float:
+    """Average ms per call of fn(i) over n back-to-back calls on the current stream."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(n):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def prepare(name: str, torch, np, b, dev):
+    """Device-resident inputs for one workload (weights quantized by the library)."""
+    from quantized_gemm_quantize_amd.inputs import bsr_from_dense, make_inputs
+    inp = make_inputs(name, seed=0)
+    x = torch.from_numpy(inp.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    wq, sw = b.w8a8_quantize_rows_f32(torch.from_numpy(inp.w).to(dev))
+    d = dict(inp=inp, x=x, wq=wq, sw=sw)
+    if inp.bs:
+        crow, col, values = bsr_from_dense(wq.cpu().numpy(), inp.block_mask, inp.bs)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        d.update(crow=t(crow), col=t(col), values=t(values))
+    return d
+
+
+def cpu_baseline(name: str, np):
+    """The CPU oracle (untuned) on a bounded sample of the same workload."""
+    import oracle
+    from quantized_gemm_quantize_amd.inputs import bsr_from_dense, make_inputs
+    inp = make_inputs(name, seed=0)
+    wq, sw = oracle.quantize_rows_f32(inp.w)
+    M, N, K = inp.M, inp.N, inp.K
+    bsr = bsr_from_dense(wq, inp.block_mask, inp.bs) if inp.bs else None
+
+    def run(rows):
+        t0 = time.perf_counter()
+        xq, sx = oracle.quantize_rows_bf16(inp.x_bits[:rows])
+        if bsr is None:
+            acc = oracle.gemm_i32(xq, wq)
+        else:
+            acc = oracle.bsr_gemm_i32(xq, *bsr, N)
+        oracle.epilogue_bf16(acc, sx, sw)
+        return time.perf_counter() - t0
+
+    probe = min(M, 64)
+    t_probe = run(probe)
+    rows = int(min(M, max(probe, probe * 15.0 / max(t_probe, 1e-6))))
+    t = run(rows)
+    ops = 2.0 * rows * N * K
+    return {"value": round(ops / t / 1e12, 6), "unit": "TOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the {name} workload (M={M}, N={N}, K={K}): "
+                      f"quantize + exact int GEMM + float64 epilogue, {t:.2f} s wall"}
+
+
+def bench_decode(torch, np, b, dev, steps, warmup):
+    """M=16 weight-streaming GEMM: GB/s with weight copies rotated past the Infinity Cache."""
+    d = prepare("decode", torch, np, b, dev)
+    M, N, K = d["inp"].M, d["inp"].N, d["inp"].K
+    xq, sx = b.w8a8_quantize_rows(d["x"])
+    R = rotation(N * K)
+    wqs = [d["wq"].clone() for _ in range(R)]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    xq2, sx2 = torch.empty_like(xq), torch.empty_like(sx)
+    gemm = lambda i: b.w8a8_gemm(xq, sx, wqs[i % R], d["sw"], out=out)
+
+    def step(i):
+        b.w8a8_quantize_rows(d["x"], xq2, sx2)
+        b.w8a8_gemm(xq2, sx2, wqs[i % R], d["sw"], out=out)
+
+    for i in range(warmup):
+        step(i)
+    ms_gemm = time_loop(gemm, steps, torch)
+    ms_step = time_loop(step, steps, torch)
+    gemm_bytes = M * K + 4 * M + N * K + 4 * N + 2 * M * N
+    layer_bytes = 2 * M * K + N * K + 4 * N + 2 * M * N
+    gbs = gemm_bytes / (ms_gemm * 1e-3) / 1e9
+    return {"workload": f"decode M={M} K={K} N={N}", "gemm_us": round(ms_gemm * 1e3, 3),
+            "gemm_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "gemm_bytes": gemm_bytes, "step_us": round(ms_step * 1e3, 3),
+            "step_GBps": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
+            "weight_copies_rotated": R}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer is "
+              "data parallel over rows, so N GPUs would each run this same kernel on M/N rows.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from quantized_gemm_quantize_amd import binding as b
+    b.load()
+    dev = torch.device("cuda:0")
+    name = args.config
+    d = prepare(name, torch, np, b, dev)
+    inp = d["inp"]
+    M, N, K = inp.M, inp.N, inp.K
+    bsr = bool(inp.bs)
+
+    # rotated input sets: X, weights and outputs at distinct addresses
+    per_set = 2 * M * K + M * K + (len(d["values"].view(-1)) if bsr else N * K) + 2 * M * N
+    R = rotation(per_set)
+    xs = [d["x"].clone() for _ in range(R)]
+    if bsr:
+        ws = [d["values"].clone() for _ in range(R)]
+    else:
+        ws = [d["wq"].clone() for _ in range(R)]
+    xqs = [torch.empty((M, K), dtype=torch.int8, device=dev) for _ in range(R)]
+    sxs = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(R)]
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+
+    def quant(i):
+        j = i % R
+        b.w8a8_quantize_rows(xs[j], xqs[j], sxs[j])
+
+    def gemm(i):
+        j = i % R
+        if bsr:
+            b.w8a8_bsr_gemm(xqs[j], sxs[j], d["crow"], d["col"], ws[j], d["sw"], out=outs[j])
+        else:
+            b.w8a8_gemm(xqs[j], sxs[j], ws[j], d["sw"], out=outs[j])
+
+    def step(i):
+        quant(i)
+        gemm(i)
+
+    for i in range(max(args.warmup, R)):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = time_loop(step, args.steps, torch)
+    ms_gemm = time_loop(gemm, args.steps, torch)
+    ms_quant = time_loop(quant, args.steps, torch)
+
+    ops = 2.0 * M * N * K
+    if bsr:
+        ops = 2.0 * M * K * 64 * int(d["values"].shape[0])   # stored blocks only
+    value = ops / (ms_step * 1e-3) / 1e12
+    gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
+    q_bytes = 2 * M * K + M * K + 4 * M
+
+    traffic = None
+    if os.path.exists(TRAFFIC_RECORD) and name == "prefill_outliers":
+        rec = json.load(open(TRAFFIC_RECORD))
+        if rec.get("source_hash") == source_hash(GEMM_SOURCES):
+            traffic = rec.get("bytes_per_launch")
+
+    if bsr:
+        gemm_bytes = M * K + 4 * M + d["values"].numel() + 4 * N + 2 * M * N
+        roof = {"bound": "hbm", "achieved": round(gemm_bytes / (ms_gemm * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        roof["frac"] = round(roof["achieved"] / PEAK_HBM_GBS, 4)
+    else:
+        roof = {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS,
+                "unit": "TOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4)}
+    roof["traffic"] = traffic
+    roof["kernel"] = "w8a8_bsr_gemm" if bsr else "w8a8_gemm"
+    roof["avg_launch_us"] = round(ms_gemm * 1e3, 3)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{name} M={M} K={K} N={N}" + (f" BSR 64x64 nnzb={d['values'].shape[0]}" if bsr else ""),
+                   "step": "w8a8_quantize_rows + " + ("w8a8_bsr_gemm" if bsr else "w8a8_gemm"),
+                   "seed": 0, "input_sets_rotated": R},
+        "roofline": roof,
+        "quantize_rows": {"us": round(ms_quant * 1e3, 3),
+                          "GBps": round(q_bytes / (ms_quant * 1e-3) / 1e9, 1),
+                          "frac_of_hbm_peak": round(q_bytes / (ms_quant * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "gemm_only": {"us": round(ms_gemm * 1e3, 3), "TOPs": round(gemm_tops, 1),
+                      "frac_of_int8_peak": round(gemm_tops / PEAK_INT8_TOPS, 4)},
+    }
+    if not args.no_decode and name == "prefill_outliers":
+        line["decode_m16"] = bench_decode(torch, np, b, dev, args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(name, np)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

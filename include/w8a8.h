@@ -1,0 +1,145 @@
+/*
+ * w8a8.h -- C ABI of libw8a8.so, the dynamically quantized int8 linear layer
+ * (W8A8) for AMD Instinct MI355X (gfx950).
+ *
+ *   out[M,N] (bf16) = bf16( (sum_k xq[m,k] * wq[n,k]) * x_scale[m] * w_scale[n] )
+ *   with xq, x_scale = quantize_rows(X) computed at run time.
+ *
+ * The layer follows the pages it was designed from:
+ *  - activations are quantized dynamically, per row, with no calibration
+ *    ("int8 dynamicquant", pytorch/ao PR #821; dynamic scaling in the vLLM
+ *    csrc/quantization log);
+ *  - a scale is the row absmax divided by 127 in binary32 (Paddle sparse_fc
+ *    PR #41770, spmm_plugin.cu weight-scale hunk), values are divided by it,
+ *    rounded half to even and clamped to [-127,127] before the cast (clamp
+ *    commit in the vLLM log);
+ *  - weights arrive already quantized, one fp32 scale per output channel, and
+ *    are owned by the caller (the same Paddle PR asks for int8 weights with the
+ *    model's own scale, channel-wise scale vectors, and no plugin-owned weight
+ *    memory so that weights can be shared);
+ *  - the product accumulates in int32 and the dequantization is fused into the
+ *    GEMM so the int32 matrix never reaches memory, with bf16 output to keep
+ *    small outputs (pytorch/ao PR #821: i8i8 -> bf16 change, the int32
+ *    materialization and fused-dequant paragraphs, the int32/bf16 out_dtype
+ *    thread);
+ *  - int8 operands are K-contiguous on both sides, A row-major and B given as
+ *    [N,K] (triton issue #634, layout answer and the 1.44 ms -> 0.286 ms fix);
+ *  - block sparsity is passed as raw crow/col/values arrays with 64x64 blocks
+ *    (pytorch/ao PR #821: custom-op paragraph, bsr_dense_addmm warning).
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing, keeps no state between calls (except the thread-local
+ *    last HIP error) and is reentrant.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without synchronizing. Outputs are valid once the
+ *    stream reaches that point.
+ *  - Arguments are validated on the host before any HIP call; a failed check
+ *    returns its code and launches nothing. M == 0 is a valid empty call that
+ *    launches nothing (pointers sized by M may then be NULL).
+ *  - Base pointers must be 16-byte aligned (W8A8_ERR_ALIGN).
+ *  - K must be a positive multiple of 16 and at most W8A8_MAX_K, so that
+ *    127*127*K < 2^31 and int32 accumulation is exact (pytorch/ao PR #821,
+ *    2**31 / 2**14 headroom remark) (W8A8_ERR_SHAPE / W8A8_ERR_K_OVERFLOW).
+ *  - A launch failure returns W8A8_ERR_HIP; w8a8_last_hip_error() then gives
+ *    the hipError_t.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W8A8_OK = 0,
+    W8A8_ERR_NULL = -1,       /* a required pointer is NULL */
+    W8A8_ERR_SHAPE = -2,      /* a size is out of range or not a required multiple */
+    W8A8_ERR_ALIGN = -3,      /* a base pointer is not 16-byte aligned */
+    W8A8_ERR_K_OVERFLOW = -4, /* K > W8A8_MAX_K: int32 accumulation could overflow */
+    W8A8_ERR_BLOCKSIZE = -5,  /* BSR block size other than 64 */
+    W8A8_ERR_DTYPE = -6,      /* unknown output dtype selector */
+    W8A8_ERR_HIP = -7         /* the HIP runtime reported an error at launch */
+} w8a8_status;
+
+typedef enum {
+    W8A8_OUT_BF16 = 0, /* out is bf16 [M,N]: the fused dequant epilogue */
+    W8A8_OUT_I32 = 1   /* out is int32 [M,N]: raw accumulators, for exactness checks */
+} w8a8_out_dtype;
+
+/* Largest K with 127*127*K < 2^31 that is a multiple of 16. */
+#define W8A8_MAX_K 133136
+
+/*
+ * Dynamic per-row quantization of bf16 activations.
+ *   x_bf16  [M,K] bf16, row-major (read)
+ *   xq      [M,K] int8, row-major (written): clamp(rint(fl32(x / s)), -127, 127)
+ *   x_scale [M]   fp32 (written): s = fl32(max_k |x[m,k]| / 127); s = 0 and
+ *           xq = 0 for an all-zero row. Division is IEEE binary32, rounding
+ *           half to even, subnormals kept. Non-finite inputs are outside the
+ *           domain (output unspecified).
+ * Errors: NULL, SHAPE (M < 0, K <= 0, K % 16), K_OVERFLOW, ALIGN, HIP.
+ */
+w8a8_status w8a8_quantize_rows(const void *x_bf16, int64_t M, int64_t K, int8_t *xq,
+                               float *x_scale, void *stream);
+
+/*
+ * The same rule on fp32 rows: per-output-channel weight preparation, W [N,K]
+ * fp32 -> wq [N,K] int8 + w_scale [N] (Paddle sparse_fc PR #41770, channel-wise
+ * weight scale discussion). Arguments and errors as w8a8_quantize_rows, with
+ * x an fp32 [M,K] row-major array.
+ */
+w8a8_status w8a8_quantize_rows_f32(const float *x, int64_t M, int64_t K, int8_t *xq,
+                                   float *x_scale, void *stream);
+
+/*
+ * Dense W8A8 GEMM with the fused dequant epilogue.
+ *   xq      [M,K] int8 row-major, x_scale [M] fp32   (from w8a8_quantize_rows)
+ *   wq      [N,K] int8, K-contiguous (one row per output channel)
+ *   w_scale [N]   fp32 per output channel
+ *   out     [M,N] row-major: bf16 = bf16_rne(acc * x_scale[m] * w_scale[n]),
+ *           or int32 acc when out_dtype == W8A8_OUT_I32.
+ * The int32 accumulators stay on chip. M >= 0 (any value; M <= 64 takes a
+ * weight-streaming path), N a positive multiple of 16.
+ * Errors: NULL, SHAPE (M < 0, N <= 0, N % 16, K <= 0, K % 16), K_OVERFLOW,
+ *         ALIGN, DTYPE, HIP.
+ */
+w8a8_status w8a8_gemm(const int8_t *xq, const float *x_scale, int64_t M, const int8_t *wq,
+                      const float *w_scale, int64_t N, int64_t K, void *out,
+                      w8a8_out_dtype out_dtype, void *stream);
+
+/*
+ * Block-sparse (BSR) W8A8 GEMM with the fused dequant epilogue: only stored
+ * weight blocks are read and multiplied; output channels of block rows with
+ * no stored block are written as +0.
+ *   xq, x_scale as for w8a8_gemm ([M,K] int8, [M] fp32)
+ *   crow    [N/bs + 1] int32: block row r owns blocks crow[r] .. crow[r+1]-1,
+ *           crow[0] = 0, non-decreasing, crow[N/bs] = nnzb
+ *   col     [nnzb] int32: block column of each stored block (< K/bs)
+ *   values  [nnzb, bs, bs] int8: values[j][i][c] = W[r*bs + i, col[j]*bs + c]
+ *           (each block row K-contiguous, like the dense [N,K] weight)
+ *   w_scale [N] fp32 per output channel, out [M,N] as for w8a8_gemm.
+ * bs must be 64; N and K positive multiples of 64; nnzb >= 0 (col and values
+ * may be NULL when nnzb == 0). Malformed index arrays (out-of-range entries,
+ * decreasing crow) give unspecified output values, but the kernel clamps every
+ * index so it never reads outside the given arrays.
+ * Errors: NULL, SHAPE, K_OVERFLOW, BLOCKSIZE, ALIGN, DTYPE, HIP.
+ */
+w8a8_status w8a8_bsr_gemm(const int8_t *xq, const float *x_scale, int64_t M, int64_t K,
+                          const int32_t *crow, const int32_t *col, const int8_t *values,
+                          int64_t nnzb, int64_t bs, const float *w_scale, int64_t N, void *out,
+                          w8a8_out_dtype out_dtype, void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *w8a8_status_string(int status);
+
+/* hipError_t value behind the calling thread's last W8A8_ERR_HIP (0 if none). */
+int w8a8_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

@@ -1,0 +1,175 @@
+"""Python binding of libw8a8.so (C ABI in include/w8a8.h): marshalling only.
+
+Each function checks tensor dtypes, shapes and devices, allocates missing
+outputs with torch.empty on the input's device, and passes raw device
+pointers plus the current HIP stream to the library function of the same
+name. All arithmetic runs in the library's kernels; there is no fallback. If
+libw8a8.so is absent, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw8a8.so")
+
+W8A8_OK = 0
+W8A8_ERR_NULL = -1
+W8A8_ERR_SHAPE = -2
+W8A8_ERR_ALIGN = -3
+W8A8_ERR_K_OVERFLOW = -4
+W8A8_ERR_BLOCKSIZE = -5
+W8A8_ERR_DTYPE = -6
+W8A8_ERR_HIP = -7
+W8A8_OUT_BF16 = 0
+W8A8_OUT_I32 = 1
+W8A8_MAX_K = 133136
+
+_lib = None
+
+
+class W8A8Error(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        lib = load()
+        msg = lib.w8a8_status_string(status).decode()
+        if status == W8A8_ERR_HIP:
+            msg += f" (hipError_t {lib.w8a8_last_hip_error()})"
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+def load():
+    """Load libw8a8.so and declare its C signatures (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.w8a8_quantize_rows.argtypes = [p, i64, i64, p, p, p]
+    lib.w8a8_quantize_rows_f32.argtypes = [p, i64, i64, p, p, p]
+    lib.w8a8_gemm.argtypes = [p, p, i64, p, p, i64, i64, p, i32, p]
+    lib.w8a8_bsr_gemm.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, p, i32, p]
+    for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_bsr_gemm"):
+        getattr(lib, fn).restype = i32
+    lib.w8a8_status_string.argtypes = [i32]
+    lib.w8a8_status_string.restype = ctypes.c_char_p
+    lib.w8a8_last_hip_error.argtypes = []
+    lib.w8a8_last_hip_error.restype = i32
+    _lib = lib
+    return lib
+
+
+def _stream_handle(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check_tensor(t: torch.Tensor, name: str, dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _call(fn: str, *args):
+    st = getattr(load(), fn)(*args)
+    if st != W8A8_OK:
+        raise W8A8Error(st, fn)
+
+
+def _quantize(fn, x, xq, x_scale, stream, dtype):
+    _check_tensor(x, "x", dtype, 2)
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check_tensor(xq, "xq", torch.int8, 2)
+    _check_tensor(x_scale, "x_scale", torch.float32, 1)
+    if tuple(xq.shape) != (M, K) or tuple(x_scale.shape) != (M,):
+        raise ValueError("output shapes")
+    _call(fn, x.data_ptr(), M, K, xq.data_ptr(), x_scale.data_ptr(), _stream_handle(stream))
+    return xq, x_scale
+
+
+def w8a8_quantize_rows(x, xq=None, x_scale=None, stream=None):
+    """bf16 [M,K] -> (int8 [M,K], fp32 [M]) per-row absmax/127 quantization."""
+    return _quantize("w8a8_quantize_rows", x, xq, x_scale, stream, torch.bfloat16)
+
+
+def w8a8_quantize_rows_f32(x, xq=None, x_scale=None, stream=None):
+    """fp32 [M,K] -> (int8 [M,K], fp32 [M]); per-output-channel weight preparation."""
+    return _quantize("w8a8_quantize_rows_f32", x, xq, x_scale, stream, torch.float32)
+
+
+def _out(out, M, N, out_dtype, device):
+    tdtype = torch.bfloat16 if out_dtype == W8A8_OUT_BF16 else torch.int32
+    if out is None:
+        out = torch.empty((M, N), dtype=tdtype, device=device)
+    _check_tensor(out, "out", tdtype, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out shape")
+    return out
+
+
+def _out_dtype(out_dtype) -> int:
+    if out_dtype in ("bf16", torch.bfloat16, W8A8_OUT_BF16):
+        return W8A8_OUT_BF16
+    if out_dtype in ("i32", torch.int32, W8A8_OUT_I32):
+        return W8A8_OUT_I32
+    raise ValueError(f"out_dtype {out_dtype!r}")
+
+
+def w8a8_gemm(xq, x_scale, wq, w_scale, out=None, out_dtype="bf16", stream=None):
+    """out [M,N] = bf16(sum_k xq[m,k] wq[n,k] * x_scale[m] * w_scale[n]) (or int32 acc)."""
+    od = _out_dtype(out_dtype)
+    _check_tensor(xq, "xq", torch.int8, 2)
+    _check_tensor(x_scale, "x_scale", torch.float32, 1)
+    _check_tensor(wq, "wq", torch.int8, 2)
+    _check_tensor(w_scale, "w_scale", torch.float32, 1)
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K2 != K or tuple(x_scale.shape) != (M,) or tuple(w_scale.shape) != (N,):
+        raise ValueError("operand shapes")
+    out = _out(out, M, N, od, xq.device)
+    _call("w8a8_gemm", xq.data_ptr(), x_scale.data_ptr(), M, wq.data_ptr(), w_scale.data_ptr(),
+          N, K, out.data_ptr(), od, _stream_handle(stream))
+    return out
+
+
+def w8a8_bsr_gemm(xq, x_scale, crow, col, values, w_scale, out=None, out_dtype="bf16",
+                  stream=None):
+    """Block-sparse W8A8 GEMM; crow [N/64+1], col [nnzb], values [nnzb,64,64] int8."""
+    od = _out_dtype(out_dtype)
+    _check_tensor(xq, "xq", torch.int8, 2)
+    _check_tensor(x_scale, "x_scale", torch.float32, 1)
+    _check_tensor(crow, "crow", torch.int32, 1)
+    _check_tensor(col, "col", torch.int32, 1)
+    _check_tensor(values, "values", torch.int8, 3)
+    _check_tensor(w_scale, "w_scale", torch.float32, 1)
+    M, K = xq.shape
+    nnzb, bs, bs2 = values.shape
+    N = w_scale.shape[0]
+    if bs != bs2 or col.shape[0] != nnzb or crow.shape[0] != N // max(bs, 1) + 1:
+        raise ValueError("BSR array shapes")
+    out = _out(out, M, N, od, xq.device)
+    _call("w8a8_bsr_gemm", xq.data_ptr(), x_scale.data_ptr(), M, K, crow.data_ptr(),
+          col.data_ptr() if nnzb else 0, values.data_ptr() if nnzb else 0, nnzb, bs,
+          w_scale.data_ptr(), N, out.data_ptr(), od, _stream_handle(stream))
+    return out
+
+
+def w8a8_linear(x, wq, w_scale, out=None, stream=None):
+    """Dynamically quantized linear layer: quantize_rows(x) then the fused GEMM."""
+    xq, xs = w8a8_quantize_rows(x, stream=stream)
+    return w8a8_gemm(xq, xs, wq, w_scale, out=out, stream=stream)

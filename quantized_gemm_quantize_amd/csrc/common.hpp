@@ -1,0 +1,51 @@
+// Device-side building blocks shared by the W8A8 kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;   // CDNA wavefront width
+constexpr int kXcds = 8;    // MI355X: 8 accelerator complex dies, 32 CUs each
+
+// int8 MFMA, 32x32 output tile, K = 32 per instruction (16 int8 per lane per
+// operand). Output layout (lane l, element r of the v16i):
+//   column = l % 32, row = 8 * (r / 4) + 4 * (l / 32) + r % 4.
+__device__ __forceinline__ v16i mfma_32x32x32(v4i a, v4i b, v16i c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// int8 MFMA, 16x16 output tile, K = 64 per instruction. Output layout
+// (lane l, element r of the v4i): column = l % 16, row = 4 * (l / 16) + r.
+__device__ __forceinline__ v4i mfma_16x16x64(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// Two floats -> two bf16 (round to nearest even; v_cvt_pk_bf16_f32 on gfx950),
+// packed into one 32-bit word, first value in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    v2f f = {lo, hi};
+    v2bf b = __builtin_convertvector(f, v2bf);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Map the hardware dispatch order (workgroup i runs on XCD i % 8) to a tile
+// order in which every XCD owns one contiguous range of tiles, so tiles that
+// share operand rows land in the same L2. A bijection on [0, tiles).
+__device__ __forceinline__ int xcd_contiguous(int pid, int tiles) {
+    const int q = tiles / kXcds, r = tiles % kXcds;
+    const int xcd = pid % kXcds, idx = pid / kXcds;
+    const int base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+    return base + idx;
+}
+
+}  // namespace w8a8

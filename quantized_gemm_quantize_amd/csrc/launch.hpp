@@ -1,0 +1,24 @@
+// Internal kernel launchers behind the C ABI (w8a8_abi.cpp). Arguments are
+// already validated when these run; each returns the HIP error of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+hipError_t launch_quantize_rows_bf16(const uint16_t *x, int64_t M, int K, int8_t *xq, float *xs,
+                                     hipStream_t stream);
+hipError_t launch_quantize_rows_f32(const float *x, int64_t M, int K, int8_t *xq, float *xs,
+                                    hipStream_t stream);
+
+// Dense GEMM: picks the weight-streaming kernel for M <= 64, the LDS-tiled
+// MFMA kernel otherwise.
+hipError_t launch_gemm(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
+                       int N, int K, void *out, bool out_i32, hipStream_t stream);
+
+hipError_t launch_bsr_gemm(const int8_t *xq, const float *xs, int M, int K, const int32_t *crow,
+                           const int32_t *col, const int8_t *values, int nnzb, const float *ws,
+                           int N, void *out, bool out_i32, hipStream_t stream);
+
+}  // namespace w8a8

@@ -1,0 +1,123 @@
+// C ABI of libw8a8.so: argument validation, then one launch on the caller's
+// stream. Declarations and argument contracts are in include/w8a8.h.
+//
+// Every check runs on the host before any HIP call, so a rejected call
+// touches no device state. Failures return a nonzero status, as the pages'
+// TensorRT plugin does with its library status (Paddle sparse_fc PR #41770,
+// spmm_plugin.cu enqueue hunk).
+#include "../../include/w8a8.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+w8a8_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return W8A8_OK;
+    g_last_hip_error = static_cast<int>(e);
+    return W8A8_ERR_HIP;
+}
+
+// K checks shared by every entry: positive multiple of 16, int32-safe.
+w8a8_status check_k(int64_t K) {
+    if (K <= 0 || K % 16 != 0) return W8A8_ERR_SHAPE;
+    if (K > W8A8_MAX_K) return W8A8_ERR_K_OVERFLOW;
+    return W8A8_OK;
+}
+
+// Sizes the kernels index with 32-bit integers.
+bool too_big(int64_t M, int64_t N) { return M > INT_MAX / 2 || N > INT_MAX / 2; }
+
+template <typename T>
+w8a8_status quantize_entry(const T *x, int64_t M, int64_t K, int8_t *xq, float *x_scale,
+                           void *stream,
+                           hipError_t (*launch)(const T *, int64_t, int, int8_t *, float *,
+                                                hipStream_t)) {
+    if (M < 0) return W8A8_ERR_SHAPE;
+    if (w8a8_status s = check_k(K)) return s;
+    if (M == 0) return W8A8_OK;
+    if (M > (int64_t)INT_MAX * 4) return W8A8_ERR_SHAPE;  // grid.x limit, 4 rows per block
+    if (!x || !xq || !x_scale) return W8A8_ERR_NULL;
+    if (misaligned(x) || misaligned(xq) || misaligned(x_scale)) return W8A8_ERR_ALIGN;
+    return hip_status(launch(x, M, (int)K, xq, x_scale, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+w8a8_status w8a8_quantize_rows(const void *x_bf16, int64_t M, int64_t K, int8_t *xq,
+                               float *x_scale, void *stream) {
+    return quantize_entry<uint16_t>(static_cast<const uint16_t *>(x_bf16), M, K, xq, x_scale,
+                                    stream, w8a8::launch_quantize_rows_bf16);
+}
+
+w8a8_status w8a8_quantize_rows_f32(const float *x, int64_t M, int64_t K, int8_t *xq,
+                                   float *x_scale, void *stream) {
+    return quantize_entry<float>(x, M, K, xq, x_scale, stream, w8a8::launch_quantize_rows_f32);
+}
+
+w8a8_status w8a8_gemm(const int8_t *xq, const float *x_scale, int64_t M, const int8_t *wq,
+                      const float *w_scale, int64_t N, int64_t K, void *out,
+                      w8a8_out_dtype out_dtype, void *stream) {
+    if (M < 0 || N <= 0 || N % 16 != 0 || too_big(M, N)) return W8A8_ERR_SHAPE;
+    if (w8a8_status s = check_k(K)) return s;
+    if (out_dtype != W8A8_OUT_BF16 && out_dtype != W8A8_OUT_I32) return W8A8_ERR_DTYPE;
+    if ((M + 127) / 128 > INT_MAX / ((N + 127) / 128)) return W8A8_ERR_SHAPE;  // grid.x
+    if (M == 0) return W8A8_OK;
+    if (!xq || !x_scale || !wq || !w_scale || !out) return W8A8_ERR_NULL;
+    if (misaligned(xq) || misaligned(x_scale) || misaligned(wq) || misaligned(w_scale) ||
+        misaligned(out))
+        return W8A8_ERR_ALIGN;
+    return hip_status(w8a8::launch_gemm(xq, x_scale, (int)M, wq, w_scale, (int)N, (int)K, out,
+                                        out_dtype == W8A8_OUT_I32,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+w8a8_status w8a8_bsr_gemm(const int8_t *xq, const float *x_scale, int64_t M, int64_t K,
+                          const int32_t *crow, const int32_t *col, const int8_t *values,
+                          int64_t nnzb, int64_t bs, const float *w_scale, int64_t N, void *out,
+                          w8a8_out_dtype out_dtype, void *stream) {
+    if (bs != 64) return W8A8_ERR_BLOCKSIZE;
+    if (M < 0 || N <= 0 || N % bs != 0 || K % bs != 0 || nnzb < 0 || too_big(M, N))
+        return W8A8_ERR_SHAPE;
+    if (w8a8_status s = check_k(K)) return s;
+    if (nnzb > (N / bs) * (K / bs)) return W8A8_ERR_SHAPE;
+    if (out_dtype != W8A8_OUT_BF16 && out_dtype != W8A8_OUT_I32) return W8A8_ERR_DTYPE;
+    if ((M + 127) / 128 > INT_MAX / (N / bs)) return W8A8_ERR_SHAPE;  // grid.x
+    if (M == 0) return W8A8_OK;
+    if (!xq || !x_scale || !crow || !w_scale || !out) return W8A8_ERR_NULL;
+    if (nnzb > 0 && (!col || !values)) return W8A8_ERR_NULL;
+    if (misaligned(xq) || misaligned(x_scale) || misaligned(crow) || misaligned(w_scale) ||
+        misaligned(out) || (nnzb > 0 && (misaligned(col) || misaligned(values))))
+        return W8A8_ERR_ALIGN;
+    return hip_status(w8a8::launch_bsr_gemm(xq, x_scale, (int)M, (int)K, crow, col, values,
+                                            (int)nnzb, w_scale, (int)N, out,
+                                            out_dtype == W8A8_OUT_I32,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+const char *w8a8_status_string(int status) {
+    switch (status) {
+        case W8A8_OK: return "ok";
+        case W8A8_ERR_NULL: return "a required pointer is NULL";
+        case W8A8_ERR_SHAPE: return "a size is out of range or not a required multiple";
+        case W8A8_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+        case W8A8_ERR_K_OVERFLOW: return "K exceeds the int32-safe bound (127*127*K < 2^31)";
+        case W8A8_ERR_BLOCKSIZE: return "BSR block size must be 64";
+        case W8A8_ERR_DTYPE: return "unknown output dtype";
+        case W8A8_ERR_HIP: return "HIP launch error (see w8a8_last_hip_error)";
+        default: return "unknown status";
+    }
+}
+
+int w8a8_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects every invalid argument with its documented status before any HIP
+call (so these calls never touch a device). Pointer arguments here are plain
+integers that are never dereferenced.
+"""
+import os
+import re
+
+import pytest
+
+from quantized_gemm_quantize_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a8.h")
+
+OK, NULL, SHAPE, ALIGN, KOVF, BLK, DTYPE = 0, -1, -2, -3, -4, -5, -6
+P = 0x10000  # an aligned, never-dereferenced stand-in for a device pointer
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libw8a8.so not built")
+    return binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w ]+?\*?\s*\b(w8a8_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_bsr_gemm",
+               "w8a8_status_string", "w8a8_last_hip_error"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for fn in declared_functions():
+        assert hasattr(lib, fn), fn
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert f"#define W8A8_MAX_K {binding.W8A8_MAX_K}" in text
+    assert 127 * 127 * binding.W8A8_MAX_K < 2 ** 31
+    assert 127 * 127 * (binding.W8A8_MAX_K + 16) >= 2 ** 31
+    for name in ("W8A8_ERR_NULL", "W8A8_ERR_SHAPE", "W8A8_ERR_ALIGN", "W8A8_ERR_K_OVERFLOW",
+                 "W8A8_ERR_BLOCKSIZE", "W8A8_ERR_DTYPE", "W8A8_ERR_HIP"):
+        m = re.search(rf"{name}\s*=\s*(-?\d+)", text)
+        assert int(m.group(1)) == getattr(binding, name)
+
+
+def test_status_strings(lib):
+    for st in (OK, NULL, SHAPE, ALIGN, KOVF, BLK, DTYPE, -7, 99):
+        assert lib.w8a8_status_string(st)
+    assert lib.w8a8_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("fn", ["w8a8_quantize_rows", "w8a8_quantize_rows_f32"])
+def test_quantize_validation(lib, fn):
+    f = getattr(lib, fn)
+    assert f(P, -1, 64, P, P, None) == SHAPE
+    assert f(P, 4, 0, P, P, None) == SHAPE
+    assert f(P, 4, 24, P, P, None) == SHAPE          # K % 16
+    assert f(P, 4, 133152, P, P, None) == KOVF
+    assert f(0, 4, 64, P, P, None) == NULL
+    assert f(P, 4, 64, 0, P, None) == NULL
+    assert f(P, 4, 64, P, 0, None) == NULL
+    assert f(P + 8, 4, 64, P, P, None) == ALIGN
+    assert f(P, 4, 64, P + 4, P, None) == ALIGN
+    assert f(P, 0, 64, 0, 0, None) == OK                # empty: no launch
+
+
+def test_gemm_validation(lib):
+    g = lib.w8a8_gemm
+    args = lambda **kw: [kw.get("xq", P), kw.get("xs", P), kw.get("M", 32), kw.get("wq", P),
+                         kw.get("ws", P), kw.get("N", 64), kw.get("K", 64), kw.get("out", P),
+                         kw.get("od", 0), None]
+    assert g(*args(M=-1)) == SHAPE
+    assert g(*args(N=0)) == SHAPE
+    assert g(*args(N=40)) == SHAPE                      # N % 16
+    assert g(*args(K=0)) == SHAPE
+    assert g(*args(K=72)) == SHAPE                      # K % 16
+    assert g(*args(K=133152)) == KOVF
+    assert g(*args(od=2)) == DTYPE
+    assert g(*args(od=-1)) == DTYPE
+    for k in ("xq", "xs", "wq", "ws", "out"):
+        assert g(*args(**{k: 0})) == NULL, k
+        assert g(*args(**{k: P + 4})) == ALIGN, k
+    assert g(*args(M=0, xq=0, xs=0, out=0)) == OK       # empty: no launch
+
+
+def test_bsr_validation(lib):
+    b = lib.w8a8_bsr_gemm
+    args = lambda **kw: [kw.get("xq", P), kw.get("xs", P), kw.get("M", 32), kw.get("K", 128),
+                         kw.get("crow", P), kw.get("col", P), kw.get("vals", P),
+                         kw.get("nnzb", 2), kw.get("bs", 64), kw.get("ws", P), kw.get("N", 128),
+                         kw.get("out", P), kw.get("od", 0), None]
+    assert b(*args(bs=32)) == BLK
+    assert b(*args(bs=128)) == BLK
+    assert b(*args(N=96)) == SHAPE                      # N % 64
+    assert b(*args(K=80)) == SHAPE                      # K % 64
+    assert b(*args(M=-1)) == SHAPE
+    assert b(*args(nnzb=-1)) == SHAPE
+    assert b(*args(nnzb=5)) == SHAPE                    # more blocks than the grid holds
+    assert b(*args(K=133184)) == KOVF
+    assert b(*args(od=3)) == DTYPE
+    for k in ("xq", "xs", "crow", "col", "vals", "ws", "out"):
+        assert b(*args(**{k: 0})) == NULL, k
+        assert b(*args(**{k: P + 2})) == ALIGN, k
+    assert b(*args(M=0, xq=0, xs=0, out=0)) == OK

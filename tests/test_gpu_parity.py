@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: quantized activations, scales and int32 accumulators bit-exact; bf16
+outputs within 1 bf16 ulp (bit patterns mapped to ordered integers). Small
+shapes span several tiles and ragged tails and are compared element by
+element; the five workloads run at full size in the launch configuration the
+benchmark uses, compared in full for quantization and on sampled rows (the
+oracle computes those rows one by one) for the products.
+"""
+import numpy as np
+import pytest
+import torch
+
+from quantized_gemm_quantize_amd.inputs import (CONFIGS, bf16_bits_to_f32, bsr_from_dense,
+                                                make_inputs, make_linear)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def b():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from quantized_gemm_quantize_amd import binding
+    binding.load()
+    return binding
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    a = a_bits.astype(np.int64)
+    c = b_bits.astype(np.int64)
+    a = np.where(a & 0x8000, -(a & 0x7FFF), a)
+    c = np.where(c & 0x8000, -(c & 0x7FFF), c)
+    return np.abs(a - c)
+
+
+def assert_bf16_close(got_bits, ref_bits, what):
+    d = ulp_distance(got_bits, ref_bits)
+    worst = int(d.max()) if d.size else 0
+    assert worst <= 1, f"{what}: {int((d > 1).sum())} outputs differ by more than 1 ulp (max {worst})"
+    return worst
+
+
+def gpu_weights(b, oracle, w: np.ndarray):
+    """Quantize W on the GPU and check it bit-exact against the oracle's."""
+    wq_ref, sw_ref = oracle.quantize_rows_f32(w)
+    wq, sw = b.w8a8_quantize_rows_f32(torch.from_numpy(w).to(DEV))
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+    assert np.array_equal(sw.cpu().numpy().view(np.uint32), sw_ref.view(np.uint32))
+    return wq, sw, wq_ref, sw_ref
+
+
+# --- quantize_rows ----------------------------------------------------------
+
+def _check_quantize(b, oracle, x_bits, what):
+    xq_ref, sx_ref = oracle.quantize_rows_bf16(x_bits)
+    xq, sx = b.w8a8_quantize_rows(to_dev_bf16(x_bits))
+    torch.cuda.synchronize()
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32)), what
+    got = xq.cpu().numpy()
+    bad = np.argwhere(got != xq_ref)
+    assert bad.size == 0, f"{what}: {len(bad)} codes differ, first at {bad[:3].tolist()}"
+    return xq, sx, xq_ref, sx_ref
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (3, 48), (5, 256), (7, 512), (9, 528), (4, 4096),
+                                 (6, 4112), (3, 8192), (2, 16400), (130, 1024)])
+def test_quantize_rows_shapes(b, oracle, M, K):
+    log(f"quantize_rows M={M} K={K}")
+    inp = make_linear(M, 16, K, seed=M * 7 + K)
+    _check_quantize(b, oracle, inp.x_bits, f"M={M} K={K}")
+
+
+def test_quantize_rows_special_rows(b, oracle):
+    log("quantize_rows special rows")
+    K = 256
+    rows = np.zeros((12, K), np.float32)
+    rng = np.random.default_rng(3)
+    rows[1] = rng.standard_normal(K) * 2.0 ** -130          # subnormal bf16 values
+    rows[2] = rng.standard_normal(K) * 1e-38                # mixed tiny normal/subnormal
+    rows[3] = rng.standard_normal(K) * 1e37                 # huge
+    rows[4, 0] = 3.234375                                   # near-tie rows (x = absmax/2)
+    rows[4, 1:] = 1.6171875
+    rows[5, 0] = 2.265625
+    rows[5, 1:] = -1.1328125
+    rows[6, 0], rows[6, 1:] = 4.5, -2.25
+    rows[7, 0], rows[7, 1:] = 4.46875, 2.234375
+    rows[8] = np.float32(-3.0)                              # constant row
+    # every bf16 absmax mantissa with x = absmax / 2 (the near-tie family)
+    am = (1.0 + np.arange(K) / 128.0).astype(np.float32)
+    rows[9] = am
+    rows[10] = am / 2
+    rows[11] = rng.standard_normal(K) * 1e-3
+    rows[11, 7] = 0.5                                       # one outlier
+    from quantized_gemm_quantize_amd.inputs import f32_to_bf16_bits
+    _check_quantize(b, oracle, f32_to_bf16_bits(rows), "special rows")
+    # the x = absmax/2 family, one row per absmax mantissa
+    fam = np.zeros((128, 16), np.float32)
+    fam[:, 0] = 2.0 + np.arange(128) / 64.0
+    fam[:, 1:] = (fam[:, 0] / 2)[:, None]
+    _check_quantize(b, oracle, f32_to_bf16_bits(fam), "near-tie family")
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill_outliers", "large_m", "bsr"])
+def test_quantize_rows_workloads(b, oracle, name):
+    log(f"quantize_rows workload {name} {CONFIGS[name]}")
+    inp = make_inputs(name)
+    _check_quantize(b, oracle, inp.x_bits, name)
+    gpu_weights(b, oracle, inp.w)
+
+
+def test_quantize_rows_empty(b):
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    xq, xs = b.w8a8_quantize_rows(x)
+    assert xq.shape == (0, 64) and xs.shape == (0,)
+
+
+# --- dense GEMM -------------------------------------------------------------
+
+GEMM_SHAPES = [
+    (1, 16, 16), (16, 128, 256), (5, 48, 80), (17, 64, 4112), (33, 32, 192), (64, 96, 512),
+    (65, 144, 160), (130, 272, 400), (257, 256, 384), (300, 528, 272), (520, 1040, 1056),
+    (1100, 2064, 272), (129, 16, 16),
+]
+
+
+def _gemm_case(b, oracle, M, N, K, seed):
+    inp = make_linear(M, N, K, seed=seed)
+    xq, sx, xq_ref, sx_ref = _check_quantize(b, oracle, inp.x_bits, f"M={M} N={N} K={K}")
+    wq, sw, wq_ref, sw_ref = gpu_weights(b, oracle, inp.w)
+    acc_ref = oracle.gemm_i32(xq_ref, wq_ref)
+    out_ref = oracle.epilogue_bf16(acc_ref, sx_ref, sw_ref)
+    acc = b.w8a8_gemm(xq, sx, wq, sw, out_dtype="i32")
+    out = b.w8a8_gemm(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    acc_np = acc.cpu().numpy()
+    bad = np.argwhere(acc_np != acc_ref)
+    assert bad.size == 0, f"int32 acc differs at {len(bad)} places, first {bad[:4].tolist()}"
+    return assert_bf16_close(bf16_bits(out), out_ref, f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_shapes(b, oracle, M, N, K):
+    log(f"gemm M={M} N={N} K={K}")
+    _gemm_case(b, oracle, M, N, K, seed=M + 3 * N + 7 * K)
+
+
+def test_gemm_extreme_values(b, oracle):
+    """All-127 operands at the largest K: the int32 accumulator's headroom."""
+    log("gemm extreme K")
+    M, N, K = 80, 32, 133136
+    xq = torch.full((M, K), 127, dtype=torch.int8, device=DEV)
+    xq[1::2] = -127
+    wq = torch.full((N, K), 127, dtype=torch.int8, device=DEV)
+    xs = torch.ones(M, dtype=torch.float32, device=DEV)
+    ws = torch.ones(N, dtype=torch.float32, device=DEV)
+    for m in (M, 16):   # tiled and weight-streaming kernels
+        acc = b.w8a8_gemm(xq[:m].contiguous(), xs[:m].contiguous(), wq, ws, out_dtype="i32")
+        torch.cuda.synchronize()
+        a = acc.cpu().numpy().astype(np.int64)
+        assert (a[0::2] == 127 * 127 * K).all() and (a[1::2] == -127 * 127 * K).all()
+
+
+def test_gemm_zero_rows_give_positive_zero(b, oracle):
+    log("gemm zero rows")
+    inp = make_linear(96, 64, 128, seed=4)
+    inp.x_bits[5] = 0
+    inp.x_bits[70] = 0
+    xq, sx, _, _ = _check_quantize(b, oracle, inp.x_bits, "zero rows")
+    wq, sw, _, _ = gpu_weights(b, oracle, inp.w)
+    for m in (96, 16):
+        out = bf16_bits(b.w8a8_gemm(xq[:m].contiguous(), sx[:m].contiguous(), wq, sw))
+        assert (out[5] == 0).all()
+        if m == 96:
+            assert (out[70] == 0).all()
+
+
+def test_gemm_empty(b):
+    xq = torch.empty((0, 64), dtype=torch.int8, device=DEV)
+    xs = torch.empty((0,), dtype=torch.float32, device=DEV)
+    wq = torch.zeros((32, 64), dtype=torch.int8, device=DEV)
+    ws = torch.ones((32,), dtype=torch.float32, device=DEV)
+    out = b.w8a8_gemm(xq, xs, wq, ws)
+    assert out.shape == (0, 32)
+
+
+def _sampled_rows(M, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(n, M), replace=False)]))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill_outliers", "large_m"])
+def test_gemm_workloads_full_size(b, oracle, name):
+    log(f"gemm workload {name} {CONFIGS[name]}")
+    inp = make_inputs(name)
+    xq, sx, xq_ref, sx_ref = _check_quantize(b, oracle, inp.x_bits, name)
+    wq, sw, wq_ref, sw_ref = gpu_weights(b, oracle, inp.w)
+    out = bf16_bits(b.w8a8_gemm(xq, sx, wq, sw))
+    acc = b.w8a8_gemm(xq, sx, wq, sw, out_dtype="i32").cpu().numpy()
+    rows = _sampled_rows(inp.M) if inp.M > 64 else np.arange(inp.M)
+    acc_ref = oracle.gemm_i32(xq_ref[rows], wq_ref)
+    assert np.array_equal(acc[rows], acc_ref)
+    out_ref = oracle.epilogue_bf16(acc_ref, sx_ref[rows], sw_ref)
+    worst = assert_bf16_close(out[rows], out_ref, name)
+    log(f"  {name}: {len(rows)} rows x {inp.N} compared, max {worst} ulp")
+    # properties that hold for every row: finite, and zero where the row is zero
+    assert np.isfinite(bf16_bits_to_f32(out)).all()
+
+
+def test_gemm_deterministic(b, oracle):
+    log("gemm determinism")
+    inp = make_inputs("prefill_outliers", M=512)
+    xq, sx = b.w8a8_quantize_rows(to_dev_bf16(inp.x_bits))
+    wq, sw = b.w8a8_quantize_rows_f32(torch.from_numpy(inp.w).to(DEV))
+    first = b.w8a8_gemm(xq, sx, wq, sw)
+    for _ in range(5):
+        again = b.w8a8_gemm(xq, sx, wq, sw)
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
+# --- block-sparse GEMM ------------------------------------------------------
+
+def _bsr_case(b, oracle, M, N, K, zero_frac, seed, rows=None):
+    inp = make_linear(M, N, K, seed=seed, bs=64, zero_frac=zero_frac)
+    xq, sx, xq_ref, sx_ref = _check_quantize(b, oracle, inp.x_bits, "bsr X")
+    wq, sw, wq_ref, sw_ref = gpu_weights(b, oracle, inp.w)
+    crow, col, values = bsr_from_dense(wq_ref, inp.block_mask, 64)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    if values.shape[0] == 0:
+        values = np.zeros((0, 64, 64), np.int8)
+    acc = b.w8a8_bsr_gemm(xq, sx, t(crow), t(col), t(values), sw, out_dtype="i32").cpu().numpy()
+    out = bf16_bits(b.w8a8_bsr_gemm(xq, sx, t(crow), t(col), t(values), sw))
+    rows = np.arange(M) if rows is None else rows
+    acc_ref = oracle.bsr_gemm_i32(xq_ref[rows], crow, col, values, N)
+    assert np.array_equal(acc[rows], acc_ref)
+    out_ref = oracle.epilogue_bf16(acc_ref, sx_ref[rows], sw_ref)
+    worst = assert_bf16_close(out[rows], out_ref, f"bsr M={M} N={N} K={K}")
+    empty = np.flatnonzero(np.diff(crow) == 0)
+    for r in empty:
+        assert (out[:, r * 64:(r + 1) * 64] == 0).all()
+    return worst, len(empty)
+
+
+@pytest.mark.parametrize("M,N,K,zf", [(1, 64, 64, 0.0), (16, 128, 128, 0.5), (129, 256, 192, 0.7),
+                                      (300, 512, 320, 0.9), (200, 192, 128, 1.0),
+                                      (64, 320, 256, 0.0)])
+def test_bsr_shapes(b, oracle, M, N, K, zf):
+    log(f"bsr M={M} N={N} K={K} zero_frac={zf}")
+    _bsr_case(b, oracle, M, N, K, zf, seed=M + N + K)
+
+
+def test_bsr_workload_full_size(b, oracle):
+    cfg = CONFIGS["bsr"]
+    log(f"bsr workload {cfg}")
+    inp_rows = _sampled_rows(cfg["M"])
+    worst, n_empty = _bsr_case(b, oracle, cfg["M"], cfg["N"], cfg["K"], cfg["zero_frac"], seed=0,
+                               rows=inp_rows)
+    log(f"  bsr: {len(inp_rows)} rows compared, max {worst} ulp, {n_empty} empty block rows")
+
+
+def test_bsr_matches_dense_gemm(b, oracle):
+    """The BSR kernel and the dense kernel on the densified weight give the same int32 result."""
+    log("bsr vs dense")
+    inp = make_linear(256, 384, 256, seed=12, bs=64, zero_frac=0.6)
+    xq, sx = b.w8a8_quantize_rows(to_dev_bf16(inp.x_bits))
+    wq, sw = b.w8a8_quantize_rows_f32(torch.from_numpy(inp.w).to(DEV))
+    crow, col, values = bsr_from_dense(wq.cpu().numpy(), inp.block_mask, 64)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    a_bsr = b.w8a8_bsr_gemm(xq, sx, t(crow), t(col), t(values), sw, out_dtype="i32")
+    a_dense = b.w8a8_gemm(xq, sx, wq, sw, out_dtype="i32")
+    assert torch.equal(a_bsr, a_dense)
