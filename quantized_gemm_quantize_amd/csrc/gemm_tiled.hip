@@ -102,9 +102,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
     const int b_frag = BM * kCPR + (wn * WN + frag_row) * kCPR;
     const int fswz = swz(frag_row);
 
-#define W8A8_GLOAD(RA, RB, k0)                                                      \
+    // Tile t walks its K stages starting at stage t % nk (integer sums do not
+    // depend on the order): rows of one tile sit a power-of-two stride apart,
+    // so without the rotation every concurrently running tile would read the
+    // same K offset, i.e. the same L2 channel.
+    const int rot = t % nk;
+#define W8A8_GLOAD(RA, RB, j)                                                       \
     {                                                                               \
-        const int koff = (kc * 16 + (k0) < K) ? (k0) : kOutOfRange;                \
+        int ks_ = (j) + rot;                                                        \
+        if (ks_ >= nk) ks_ -= nk;                                                   \
+        const int koff = ((j) < nk && kc * 16 + ks_ * kBK < K) ? ks_ * kBK : kOutOfRange; \
         _Pragma("unroll") for (int i = 0; i < A_LD; ++i)                            \
             RA[i] = buffer_load16(ra_rsrc, voff0 + i * kRowsPerPass * K + koff);     \
         _Pragma("unroll") for (int i = 0; i < B_LD; ++i)                            \
@@ -117,44 +124,80 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
         _Pragma("unroll") for (int i = 0; i < B_LD; ++i)                            \
             s_[BM * kCPR + i * kThreads] = RB[i];                                   \
     }
-#define W8A8_COMPUTE(stage)                                                         \
+#define W8A8_FRAGS(F, S, kk)                                                        \
     {                                                                               \
-        const uint4 *S = lds + (stage) * STAGE;                                     \
-        _Pragma("unroll") for (int kk = 0; kk < kCPR / 2; ++kk) {                   \
-            const int c = (kk * 2 + half) ^ fswz;                                   \
-            v4i xa[TM], wb[TN];                                                     \
-            _Pragma("unroll") for (int i = 0; i < TM; ++i)                          \
-                xa[i] = __builtin_bit_cast(v4i, S[a_frag + i * 32 * kCPR + c]);     \
-            _Pragma("unroll") for (int j = 0; j < TN; ++j)                          \
-                wb[j] = __builtin_bit_cast(v4i, S[b_frag + j * 32 * kCPR + c]);     \
-            _Pragma("unroll") for (int i = 0; i < TM; ++i)                          \
-                _Pragma("unroll") for (int j = 0; j < TN; ++j)                      \
-                    acc[i][j] = mfma_32x32x32(wb[j], xa[i], acc[i][j]);             \
+        const int c_ = ((kk) * 2 + half) ^ fswz;                                    \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                              \
+            xa[F][i] = __builtin_bit_cast(v4i, S[a_frag + i * 32 * kCPR + c_]);     \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                              \
+            wb[F][j] = __builtin_bit_cast(v4i, S[b_frag + j * 32 * kCPR + c_]);     \
+    }
+    // MFMA slots of one stage: (TM*TN) per K step, 4 K steps. Memory work per
+    // stage: A_LD+B_LD buffer loads, 3 x (TM+TN) fragment reads, A_LD+B_LD
+    // LDS writes. Loads go one per MFMA in the first half, reads one per MFMA
+    // through the first three K steps, writes one per MFMA in the second half.
+    constexpr int NMF = 4 * TM * TN, NLD = A_LD + B_LD, NRD = 3 * (TM + TN);
+#define W8A8_SCHEDULE()                                                             \
+    {                                                                               \
+        _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                           \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
+            if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         \
+            if (q < NLD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         \
+            if (q >= NMF - NLD) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  \
         }                                                                           \
     }
-
+    // One stage: the fragments of K step kk+1 are read while step kk multiplies,
+    // the global loads for two stages ahead and the LDS writes of the stage
+    // after next are spread one per MFMA. A wavefront issues in order, so a
+    // burst of buffer loads would hold the MFMAs behind a full address queue;
+    // the scheduling-group barriers below fix the interleaving.
+#define W8A8_STAGE(stage, RA_NEXT, RB_NEXT, j_next, RA_ST, RB_ST, st_stage)          \
+    {                                                                               \
+        const uint4 *S = lds + (stage) * STAGE;                                     \
+        __builtin_amdgcn_sched_barrier(0);                                          \
+        W8A8_GLOAD(RA_NEXT, RB_NEXT, j_next)                                        \
+        _Pragma("unroll") for (int kk = 0; kk < kCPR / 2; ++kk) {                   \
+            if (kk + 1 < kCPR / 2) W8A8_FRAGS((kk + 1) & 1, S, kk + 1)              \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i)                          \
+                _Pragma("unroll") for (int j = 0; j < TN; ++j)                      \
+                    acc[i][j] = mfma_32x32x32(wb[kk & 1][j], xa[kk & 1][i], acc[i][j]); \
+        }                                                                           \
+        W8A8_LSTORE(RA_ST, RB_ST, st_stage)                                         \
+        W8A8_SCHEDULE()                                                             \
+        __builtin_amdgcn_sched_barrier(0);                                          \
+        __syncthreads();                                                            \
+        W8A8_FRAGS(0, (lds + (st_stage) * STAGE), 0)                                \
+    }
     // Stages alternate between LDS buffers 0/1 and register sets 0/1. Loads of
     // stages past K return zeros (out-of-range offsets) and land in a buffer
     // no one reads, so the loop body needs no branches.
+    v4i xa[2][TM], wb[2][TN];
     W8A8_GLOAD(ra0, rb0, 0)
-    W8A8_GLOAD(ra1, rb1, kBK)
+    W8A8_GLOAD(ra1, rb1, 1)
     W8A8_LSTORE(ra0, rb0, 0)
     __syncthreads();
+    W8A8_FRAGS(0, lds, 0)
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
-        W8A8_GLOAD(ra0, rb0, (kt + 2) * kBK)
-        W8A8_COMPUTE(0)
-        W8A8_LSTORE(ra1, rb1, 1)
-        __syncthreads();
-        W8A8_GLOAD(ra1, rb1, (kt + 3) * kBK)
-        W8A8_COMPUTE(1)
-        W8A8_LSTORE(ra0, rb0, 0)
-        __syncthreads();
+        W8A8_STAGE(0, ra0, rb0, kt + 2, ra1, rb1, 1)
+        W8A8_STAGE(1, ra1, rb1, kt + 3, ra0, rb0, 0)
     }
-    if (kt < nk) W8A8_COMPUTE(0)
+    if (kt < nk) {
+        const uint4 *S = lds;
+#pragma unroll
+        for (int kk = 0; kk < kCPR / 2; ++kk) {
+            if (kk > 0) W8A8_FRAGS(0, S, kk)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x32(wb[0][j], xa[0][i], acc[i][j]);
+        }
+    }
 #undef W8A8_GLOAD
 #undef W8A8_LSTORE
-#undef W8A8_COMPUTE
+#undef W8A8_FRAGS
+#undef W8A8_STAGE
+#undef W8A8_SCHEDULE
 
     // Tile (i, j), element r of a lane: row m = i*32 + lane%32 of the wave's
     // sub-tile, channel n = j*32 + 8*(r/4) + 4*half + r%4.

@@ -5,7 +5,7 @@
 // touches no device state. Failures return a nonzero status, as the pages'
 // TensorRT plugin does with its library status (Paddle sparse_fc PR #41770,
 // spmm_plugin.cu enqueue hunk).
-#include "../../include/w8a8.h"
+#include "w8a8.h"
 
 #include <hip/hip_runtime.h>
 
