@@ -12,15 +12,19 @@
 // Shape of the kernel (gfx950):
 //  - a workgroup of 4 wavefronts computes a BM x BN tile; each wavefront owns a
 //    (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 32x32 v_mfma_i32_32x32x32_i8 tiles;
-//  - K advances 128 bytes per stage. Every thread moves 16-byte chunks with
-//    buffer loads into registers, then into one of two LDS stages; with two
-//    register sets the loads for stage k+2 are in flight while stage k feeds
-//    the MFMAs and stage k+1 waits in registers.
-//    Buffer loads return zero past the end of the tile's rows, which handles
-//    ragged M and N without branches; a chunk past K is pointed out of range;
+//  - operands travel global -> LDS with global_load_lds_dwordx4 (gfx950's
+//    16-byte direct-to-LDS load), never through registers: on MI355X this
+//    path moves about twice the bytes per CU per clock of loads into VGPRs,
+//    which is what an int8 tile needs to keep the MFMAs fed. K advances 128
+//    bytes per stage through a ring of STAGES LDS buffers, loads running
+//    STAGES-1 stages ahead of the MFMAs;
 //  - LDS rows are 128 bytes; chunk c of row r sits at slot
 //    c ^ (r % 8) ^ ((r / 8) % 2), so 16 consecutive lanes reading the same
-//    chunk of 16 consecutive rows hit 16 distinct 16-byte bank groups;
+//    chunk of 16 consecutive rows hit 16 distinct 16-byte bank groups. A
+//    direct-to-LDS load writes 64 consecutive slots, so each lane fetches the
+//    global chunk that belongs in its slot;
+//  - rows past M or N are read from the last valid row (their outputs are
+//    never stored); chunks past K are not loaded but zeroed in LDS;
 //  - the MFMA takes the weight fragment as its first operand, so each lane
 //    ends with 4 consecutive output channels of one row: the epilogue scales
 //    them, packs 4 bf16 into 8 bytes and stages the tile in LDS, from where
@@ -34,36 +38,161 @@ namespace w8a8 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
 constexpr int kBK = 128;          // K bytes per stage
 constexpr int kCPR = kBK / 16;    // 16-byte chunks per tile row
-constexpr int kRowsPerPass = kThreads / kCPR;  // 32 tile rows per load pass
 constexpr int kGroupM = 8;
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
-constexpr int kOutOfRange = 0x40000000; // offset past every tile buffer: loads return 0
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
 
 // bank-group swizzle of a 128-byte LDS row
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const int8_t *base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(base), (short)0, bytes, kRsrcWord3);
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt bits
+// [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voffset) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
+// Workgroup barrier of the mainloop: this wavefront's loads up to the last
+// N are in LDS and its own LDS accesses are done, then all wavefronts meet.
+// No memory fence: a workgroup release fence would also wait for the
+// direct-to-LDS loads still in flight for later stages. The empty asm
+// statements keep the compiler from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_I32>
+// Per-lane load geometry of one tile: load l of this wavefront fills LDS slots
+// [wslot + 256 l, +64) (A) or [BM*kCPR + wslot + 256 l, +64) (B), i.e. tile
+// rows 8 wave + 32 l + lane/8 at physical slot lane % 8, which holds the
+// logical chunk kc = (lane % 8) ^ swz(row) -- the same for every l.
+template <int A_LD, int B_LD>
+struct TileLoads {
+    int aoff[A_LD], boff[B_LD];  // byte offsets of this lane's chunks in the tile rows
+    int kc;                      // logical chunk
+    int wslot;                   // 64 * wavefront
+    int K, nk;
+};
+
+// Issue the direct-to-LDS loads of K stage j into `wr` (or, with KTAIL, zero
+// the slots whose chunk lies past K).
+template <int BM, int A_LD, int B_LD, bool KTAIL>
+__device__ __forceinline__ void load_stage(const int8_t *__restrict__ at, const int8_t *__restrict__ bt,
+                                           uint4 *__restrict__ wr, const TileLoads<A_LD, B_LD> &g,
+                                           int j, int lane) {
+    const int k0 = j * kBK;
+    const bool in = !KTAIL || g.kc * 16 + k0 < g.K;
+#pragma unroll
+    for (int l = 0; l < A_LD + B_LD; ++l) {
+        uint4 *dst = wr + g.wslot + (l < A_LD ? 256 * l : BM * kCPR + 256 * (l - A_LD));
+        const int8_t *src = l < A_LD ? at + g.aoff[l] + k0 : bt + g.boff[l - A_LD] + k0;
+        if (in)
+            __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)dst, 16, 0, 0);
+        else
+            dst[lane] = make_uint4(0, 0, 0, 0);
+    }
+}
+
+// One K stage: multiply the stage held in `rd` while loading the stage
+// STAGES-1 ahead into `wr`, then read the first fragments of the next stage
+// from `nx`. The buffers are distinct, and the restrict qualifiers say so:
+// after inlining, the fragment reads carry alias scopes that separate them
+// from the loads still landing in `wr`, so the wait before the barrier
+// covers only the stage that has to be complete.
+//
+// Per K step kk: TM*TN MFMA slots, each followed by one memory instruction --
+// the fragment reads of step kk+1 first, then this step's share of the
+// direct-to-LDS loads. The order is pinned with scheduling barriers: a
+// wavefront issues in order, and a burst of loads or reads would hold the
+// MFMAs.
+template <int BM, int TM, int TN, int STAGES, int A_LD, int B_LD, bool KTAIL>
+__device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
+                                               const int8_t *__restrict__ bt,
+                                               const uint4 *__restrict__ rd, uint4 *__restrict__ wr,
+                                               const uint4 *__restrict__ nx,
+                                               const TileLoads<A_LD, B_LD> &g, int s, int lane,
+                                               int a_frag, int b_frag, int half, int fswz,
+                                               v16i (&acc)[TM][TN], v4i (&xa)[2][TM],
+                                               v4i (&wb)[2][TN]) {
+    constexpr int NLD = A_LD + B_LD;
+    constexpr int NMF = TM * TN;        // MFMAs per K step
+    constexpr int NRD = TM + TN;        // fragment reads per K step
+    constexpr int LPK = (NLD + 3) / 4;  // loads per K step
+    static_assert(NRD + LPK <= NMF + 2, "memory slots per K step");
+    const int j_ahead = s + STAGES - 1;
+    const bool ahead = j_ahead < g.nk;  // uniform
+    const int k0 = j_ahead * kBK;
+    const bool in = !KTAIL || g.kc * 16 + k0 < g.K;
+#pragma unroll
+    for (int kk = 0; kk < kCPR / 2; ++kk) {
+        const int f = kk & 1;
+        const int ch = ((kk + 1) * 2 + half) ^ fswz;
+#pragma unroll
+        for (int q = 0; q < NMF + 2; ++q) {
+            if (q < NMF) {
+                const int i = q / TN, j = q % TN;
+                acc[i][j] = mfma_32x32x32(wb[f][j], xa[f][i], acc[i][j]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (kk + 1 < kCPR / 2 && q < NRD) {
+                if (q < TM)
+                    xa[f ^ 1][q] = __builtin_bit_cast(v4i, rd[a_frag + q * 32 * kCPR + ch]);
+                else
+                    wb[f ^ 1][q - TM] = __builtin_bit_cast(v4i, rd[b_frag + (q - TM) * 32 * kCPR + ch]);
+            }
+            const int l = kk * LPK + (q - NRD);
+            if (q >= NRD && q < NRD + LPK && l < NLD && ahead) {
+                uint4 *dst = wr + g.wslot + (l < A_LD ? 256 * l : BM * kCPR + 256 * (l - A_LD));
+                const int8_t *src = l < A_LD ? at + g.aoff[l] + k0 : bt + g.boff[l - A_LD] + k0;
+                if (in)
+                    __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)dst, 16, 0, 0);
+                else
+                    dst[lane] = make_uint4(0, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // the next stage has landed from this wavefront (only the stage just
+    // issued may still be in flight); the barrier makes it complete for all,
+    // and frees this stage's buffer for reuse
+    if (ahead)
+        stage_barrier<(STAGES - 2) * NLD>();
+    else
+        stage_barrier<0>();
+    // with double buffering the next stage is the one just loaded into `wr`
+    // (and `nx` is not accessed), otherwise it is `nx`
+    const uint4 *next = STAGES == 2 ? wr : nx;
+    const int ch0 = half ^ fswz;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) xa[0][i] = __builtin_bit_cast(v4i, next[a_frag + i * 32 * kCPR + ch0]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) wb[0][j] = __builtin_bit_cast(v4i, next[b_frag + j * 32 * kCPR + ch0]);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool KTAIL, bool OUT_I32>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ sa, const int8_t *__restrict__ B,
     const float *__restrict__ sb, void *__restrict__ out, int M, int N, int K, int tiles_m,
     int tiles_n) {
-    static_assert(WAVES_M * WAVES_N == kThreads / kWave, "4 wavefronts");
+    static_assert(WAVES_M * WAVES_N == kWaves, "4 wavefronts");
+    static_assert(STAGES == 2 || STAGES == 3, "double or triple buffering");
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
-    constexpr int A_LD = BM / kRowsPerPass, B_LD = BN / kRowsPerPass;
+    // direct-to-LDS loads per wavefront per stage: each covers 8 tile rows
+    constexpr int A_LD = BM / (8 * kWaves), B_LD = BN / (8 * kWaves);
+    constexpr int NLD = A_LD + B_LD;
     constexpr int STAGE = (BM + BN) * kCPR;  // uint4 slots per stage
-    static_assert(BM * BN * 2 <= 2 * STAGE * 16, "bf16 tile fits in the stage buffers");
-    __shared__ uint4 lds[2 * STAGE];
+    static_assert(BM * BN * 2 <= STAGES * STAGE * 16, "bf16 tile fits in the stage buffers");
+    __shared__ uint4 lds[STAGES * STAGE];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -76,128 +205,77 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
     const int gsize = min(tiles_m - first_m, kGroupM);
     const int m0 = (first_m + (t % per_group) % gsize) * BM;
     const int n0 = ((t % per_group) / gsize) * BN;
+    const int8_t *at = A + (int64_t)m0 * K;
+    const int8_t *bt = B + (int64_t)n0 * K;
 
-    const __amdgpu_buffer_rsrc_t ra_rsrc = tile_rsrc(A + (int64_t)m0 * K, min(BM, M - m0) * K);
-    const __amdgpu_buffer_rsrc_t rb_rsrc = tile_rsrc(B + (int64_t)n0 * K, min(BN, N - n0) * K);
+    TileLoads<A_LD, B_LD> g;
+    {
+        const int lrow = 8 * wave + (lane >> 3);
+        g.kc = (lane & 7) ^ swz(lrow);
+        const int a_last = min(BM, M - m0) - 1, b_last = min(BN, N - n0) - 1;
+#pragma unroll
+        for (int l = 0; l < A_LD; ++l) g.aoff[l] = min(lrow + 32 * l, a_last) * K + g.kc * 16;
+#pragma unroll
+        for (int l = 0; l < B_LD; ++l) g.boff[l] = min(lrow + 32 * l, b_last) * K + g.kc * 16;
+        g.wslot = 64 * wave;
+        g.K = K;
+        g.nk = (K + kBK - 1) / kBK;
+    }
+    const int nk = g.nk;
 
-    // this thread loads chunk kc of tile rows lrow + 32 * i
-    const int kc = tid % kCPR, lrow = tid / kCPR;
-    const int voff0 = lrow * K + kc * 16;
-    const int slot0 = lrow * kCPR + (kc ^ swz(lrow));  // + 256 * i (32 rows keep the swizzle)
-
-    // two register sets: the loads for stage k+2 are issued while stage k is
-    // multiplied, so each load has two stages of MFMA work to arrive
-    uint4 ra0[A_LD], rb0[B_LD], ra1[A_LD], rb1[B_LD];
     v16i acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = v16i{};
 
-    const int nk = (K + kBK - 1) / kBK;
     // fragment reads: lanes 0-31 take the first 16 bytes of each 32-byte K step,
     // lanes 32-63 the second, for both operands
     const int frag_row = lane & 31, half = lane >> 5;
     const int a_frag = (wm * WM + frag_row) * kCPR;
     const int b_frag = BM * kCPR + (wn * WN + frag_row) * kCPR;
     const int fswz = swz(frag_row);
-
-    // Tile t walks its K stages starting at stage t % nk (integer sums do not
-    // depend on the order): rows of one tile sit a power-of-two stride apart,
-    // so without the rotation every concurrently running tile would read the
-    // same K offset, i.e. the same L2 channel.
-    const int rot = t % nk;
-#define W8A8_GLOAD(RA, RB, j)                                                       \
-    {                                                                               \
-        int ks_ = (j) + rot;                                                        \
-        if (ks_ >= nk) ks_ -= nk;                                                   \
-        const int koff = ((j) < nk && kc * 16 + ks_ * kBK < K) ? ks_ * kBK : kOutOfRange; \
-        _Pragma("unroll") for (int i = 0; i < A_LD; ++i)                            \
-            RA[i] = buffer_load16(ra_rsrc, voff0 + i * kRowsPerPass * K + koff);     \
-        _Pragma("unroll") for (int i = 0; i < B_LD; ++i)                            \
-            RB[i] = buffer_load16(rb_rsrc, voff0 + i * kRowsPerPass * K + koff);     \
-    }
-#define W8A8_LSTORE(RA, RB, stage)                                                  \
-    {                                                                               \
-        uint4 *s_ = lds + (stage) * STAGE + slot0;                                  \
-        _Pragma("unroll") for (int i = 0; i < A_LD; ++i) s_[i * kThreads] = RA[i];  \
-        _Pragma("unroll") for (int i = 0; i < B_LD; ++i)                            \
-            s_[BM * kCPR + i * kThreads] = RB[i];                                   \
-    }
-#define W8A8_FRAGS(F, S, kk)                                                        \
-    {                                                                               \
-        const int c_ = ((kk) * 2 + half) ^ fswz;                                    \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i)                              \
-            xa[F][i] = __builtin_bit_cast(v4i, S[a_frag + i * 32 * kCPR + c_]);     \
-        _Pragma("unroll") for (int j = 0; j < TN; ++j)                              \
-            wb[F][j] = __builtin_bit_cast(v4i, S[b_frag + j * 32 * kCPR + c_]);     \
-    }
-    // MFMA slots of one stage: (TM*TN) per K step, 4 K steps. Memory work per
-    // stage: A_LD+B_LD buffer loads, 3 x (TM+TN) fragment reads, A_LD+B_LD
-    // LDS writes. Loads go one per MFMA in the first half, reads one per MFMA
-    // through the first three K steps, writes one per MFMA in the second half.
-    constexpr int NMF = 4 * TM * TN, NLD = A_LD + B_LD, NRD = 3 * (TM + TN);
-#define W8A8_SCHEDULE()                                                             \
-    {                                                                               \
-        _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                           \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
-            if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         \
-            if (q < NLD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         \
-            if (q >= NMF - NLD) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  \
-        }                                                                           \
-    }
-    // One stage: the fragments of K step kk+1 are read while step kk multiplies,
-    // the global loads for two stages ahead and the LDS writes of the stage
-    // after next are spread one per MFMA. A wavefront issues in order, so a
-    // burst of buffer loads would hold the MFMAs behind a full address queue;
-    // the scheduling-group barriers below fix the interleaving.
-#define W8A8_STAGE(stage, RA_NEXT, RB_NEXT, j_next, RA_ST, RB_ST, st_stage)          \
-    {                                                                               \
-        const uint4 *S = lds + (stage) * STAGE;                                     \
-        __builtin_amdgcn_sched_barrier(0);                                          \
-        W8A8_GLOAD(RA_NEXT, RB_NEXT, j_next)                                        \
-        _Pragma("unroll") for (int kk = 0; kk < kCPR / 2; ++kk) {                   \
-            if (kk + 1 < kCPR / 2) W8A8_FRAGS((kk + 1) & 1, S, kk + 1)              \
-            _Pragma("unroll") for (int i = 0; i < TM; ++i)                          \
-                _Pragma("unroll") for (int j = 0; j < TN; ++j)                      \
-                    acc[i][j] = mfma_32x32x32(wb[kk & 1][j], xa[kk & 1][i], acc[i][j]); \
-        }                                                                           \
-        W8A8_LSTORE(RA_ST, RB_ST, st_stage)                                         \
-        W8A8_SCHEDULE()                                                             \
-        __builtin_amdgcn_sched_barrier(0);                                          \
-        __syncthreads();                                                            \
-        W8A8_FRAGS(0, (lds + (st_stage) * STAGE), 0)                                \
-    }
-    // Stages alternate between LDS buffers 0/1 and register sets 0/1. Loads of
-    // stages past K return zeros (out-of-range offsets) and land in a buffer
-    // no one reads, so the loop body needs no branches.
     v4i xa[2][TM], wb[2][TN];
-    W8A8_GLOAD(ra0, rb0, 0)
-    W8A8_GLOAD(ra1, rb1, 1)
-    W8A8_LSTORE(ra0, rb0, 0)
-    __syncthreads();
-    W8A8_FRAGS(0, lds, 0)
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        W8A8_STAGE(0, ra0, rb0, kt + 2, ra1, rb1, 1)
-        W8A8_STAGE(1, ra1, rb1, kt + 3, ra0, rb0, 0)
+
+    uint4 *const b0 = lds, *const b1 = lds + STAGE, *const b2 = lds + (STAGES > 2 ? 2 : 0) * STAGE;
+    // prologue: stages 0 .. STAGES-2 in flight, stage 0 landed everywhere
+    load_stage<BM, A_LD, B_LD, KTAIL>(at, bt, b0, g, 0, lane);
+    if (STAGES == 3 && nk > 1) load_stage<BM, A_LD, B_LD, KTAIL>(at, bt, b1, g, 1, lane);
+    if (STAGES == 3 && nk > 1)
+        stage_barrier<NLD>();
+    else
+        stage_barrier<0>();
+    {
+        const int ch0 = half ^ fswz;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) xa[0][i] = __builtin_bit_cast(v4i, b0[a_frag + i * 32 * kCPR + ch0]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) wb[0][j] = __builtin_bit_cast(v4i, b0[b_frag + j * 32 * kCPR + ch0]);
     }
-    if (kt < nk) {
-        const uint4 *S = lds;
-#pragma unroll
-        for (int kk = 0; kk < kCPR / 2; ++kk) {
-            if (kk > 0) W8A8_FRAGS(0, S, kk)
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x32(wb[0][j], xa[0][i], acc[i][j]);
+
+#define W8A8_STAGE(RD, WR, NX, S_)                                                          \
+    mainloop_stage<BM, TM, TN, STAGES, A_LD, B_LD, KTAIL>(at, bt, RD, WR, NX, g, S_, lane, \
+                                                          a_frag, b_frag, half, fswz, acc, xa, wb)
+    int s = 0;
+    if constexpr (STAGES == 3) {
+        for (; s + 3 <= nk; s += 3) {
+            W8A8_STAGE(b0, b2, b1, s);
+            W8A8_STAGE(b1, b0, b2, s + 1);
+            W8A8_STAGE(b2, b1, b0, s + 2);
         }
+        if (s < nk) W8A8_STAGE(b0, b2, b1, s++);
+        if (s < nk) W8A8_STAGE(b1, b0, b2, s++);
+    } else {
+        // double buffering: the buffer being filled is also the next one read
+        for (; s + 2 <= nk; s += 2) {
+            W8A8_STAGE(b0, b1, b1, s);
+            W8A8_STAGE(b1, b0, b0, s + 1);
+        }
+        if (s < nk) W8A8_STAGE(b0, b1, b1, s++);
     }
-#undef W8A8_GLOAD
-#undef W8A8_LSTORE
-#undef W8A8_FRAGS
 #undef W8A8_STAGE
-#undef W8A8_SCHEDULE
+    (void)NLD;
+    __syncthreads();  // all fragment reads done before the epilogue reuses LDS
 
     // Tile (i, j), element r of a lane: row m = i*32 + lane%32 of the wave's
     // sub-tile, channel n = j*32 + 8*(r/4) + 4*half + r%4.
@@ -264,17 +342,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-hipError_t launch_cfg(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
-                      int N, int K, void *out, bool out_i32, hipStream_t stream) {
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool KTAIL>
+void launch_tail(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
+                 int N, int K, void *out, bool out_i32, hipStream_t stream) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
     if (out_i32)
-        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, true>
+        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, KTAIL, true>
             <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, tiles_m, tiles_n);
     else
-        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, false>
+        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, KTAIL, false>
             <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, tiles_m, tiles_n);
+}
+
+// K % 128 != 0 takes the variant that zeroes the chunks past K.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+hipError_t launch_cfg(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
+                      int N, int K, void *out, bool out_i32, hipStream_t stream) {
+    if (K % kBK == 0)
+        launch_tail<BM, BN, WAVES_M, WAVES_N, STAGES, false>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
+    else
+        launch_tail<BM, BN, WAVES_M, WAVES_N, STAGES, true>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
     return hipGetLastError();
 }
 
@@ -291,9 +379,9 @@ hipError_t launch_gemm(const int8_t *xq, const float *xs, int M, const int8_t *w
     // halves LDS traffic per MFMA. Otherwise 256x128 (or 128x128) tiles.
     const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
     const long t128 = (long)((M + 255) / 256) * ((N + 127) / 128);
-    if (t256 >= 4 * 256) return launch_cfg<256, 256, 2, 2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
-    if (t128 >= 256) return launch_cfg<256, 128, 2, 2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
-    return launch_cfg<128, 128, 2, 2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
+    if (t256 >= 4 * 256) return launch_cfg<256, 256, 2, 2, 2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
+    if (t128 >= 256) return launch_cfg<256, 128, 2, 2, 3>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
+    return launch_cfg<128, 128, 2, 2, 2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
 }
 
 }  // namespace w8a8
