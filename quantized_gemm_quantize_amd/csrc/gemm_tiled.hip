@@ -103,17 +103,22 @@ __device__ __forceinline__ void load_stage(const int8_t *__restrict__ at, const 
 }
 
 // One K stage: multiply the stage held in `rd` while loading the stage
-// STAGES-1 ahead into `wr`, then read the first fragments of the next stage
+// STAGES-1 ahead into `wr`, and read the first fragments of the next stage
 // from `nx`. The buffers are distinct, and the restrict qualifiers say so:
 // after inlining, the fragment reads carry alias scopes that separate them
-// from the loads still landing in `wr`, so the wait before the barrier
-// covers only the stage that has to be complete.
+// from the loads still landing in `wr`, so the wait before the barrier covers
+// only the stage that has to be complete.
+//
+// The barrier sits before the last K step, not at the end of the stage: by
+// then every wavefront has read all of this stage's fragments, so the buffer
+// may be refilled, and the next stage's first fragments are read while the
+// last K step multiplies instead of after a barrier with nothing to overlap.
 //
 // Per K step kk: TM*TN MFMA slots, each followed by one memory instruction --
-// the fragment reads of step kk+1 first, then this step's share of the
-// direct-to-LDS loads. The order is pinned with scheduling barriers: a
-// wavefront issues in order, and a burst of loads or reads would hold the
-// MFMAs.
+// the fragment reads for the next step first, then this step's share of the
+// direct-to-LDS loads (steps 0-2). The order is pinned with scheduling
+// barriers: a wavefront issues in order, and a burst of loads or reads would
+// hold the MFMAs.
 template <int BM, int TM, int TN, int STAGES, int A_LD, int B_LD, bool KTAIL>
 __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
                                                const int8_t *__restrict__ bt,
@@ -126,31 +131,45 @@ __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
     constexpr int NLD = A_LD + B_LD;
     constexpr int NMF = TM * TN;        // MFMAs per K step
     constexpr int NRD = TM + TN;        // fragment reads per K step
-    constexpr int LPK = (NLD + 3) / 4;  // loads per K step
-    static_assert(NRD + LPK <= NMF + 2, "memory slots per K step");
+    constexpr int KS = kCPR / 2;        // K steps per stage
+    constexpr int LPK = (NLD + KS - 2) / (KS - 1);  // loads per K step, steps 0..KS-2
+    constexpr int NSLOT = NMF + 2 > NRD + LPK ? NMF + 2 : NRD + LPK;
     const int j_ahead = s + STAGES - 1;
     const bool ahead = j_ahead < g.nk;  // uniform
     const int k0 = j_ahead * kBK;
     const bool in = !KTAIL || g.kc * 16 + k0 < g.K;
+    // with double buffering the next stage is the one being loaded into `wr`
+    // (and `nx` is not accessed), otherwise it is `nx`
+    const uint4 *next = STAGES == 2 ? wr : nx;
 #pragma unroll
-    for (int kk = 0; kk < kCPR / 2; ++kk) {
+    for (int kk = 0; kk < KS; ++kk) {
         const int f = kk & 1;
-        const int ch = ((kk + 1) * 2 + half) ^ fswz;
+        if (kk == KS - 1) {
+            // the next stage has landed from this wavefront (only the stage
+            // issued in this one may still be in flight), this wavefront's
+            // reads of this stage are done; after the barrier both hold for all
+            if (ahead)
+                stage_barrier<(STAGES - 2) * NLD>();
+            else
+                stage_barrier<0>();
+        }
+        const uint4 *src_buf = kk + 1 < KS ? rd : next;
+        const int ch = (((kk + 1) % KS) * 2 + half) ^ fswz;
 #pragma unroll
-        for (int q = 0; q < NMF + 2; ++q) {
+        for (int q = 0; q < NSLOT; ++q) {
             if (q < NMF) {
                 const int i = q / TN, j = q % TN;
                 acc[i][j] = mfma_32x32x32(wb[f][j], xa[f][i], acc[i][j]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (kk + 1 < kCPR / 2 && q < NRD) {
+            if (q < NRD) {
                 if (q < TM)
-                    xa[f ^ 1][q] = __builtin_bit_cast(v4i, rd[a_frag + q * 32 * kCPR + ch]);
+                    xa[f ^ 1][q] = __builtin_bit_cast(v4i, src_buf[a_frag + q * 32 * kCPR + ch]);
                 else
-                    wb[f ^ 1][q - TM] = __builtin_bit_cast(v4i, rd[b_frag + (q - TM) * 32 * kCPR + ch]);
+                    wb[f ^ 1][q - TM] = __builtin_bit_cast(v4i, src_buf[b_frag + (q - TM) * 32 * kCPR + ch]);
             }
             const int l = kk * LPK + (q - NRD);
-            if (q >= NRD && q < NRD + LPK && l < NLD && ahead) {
+            if (kk + 1 < KS && q >= NRD && q < NRD + LPK && l < NLD && ahead) {
                 uint4 *dst = wr + g.wslot + (l < A_LD ? 256 * l : BM * kCPR + 256 * (l - A_LD));
                 const int8_t *src = l < A_LD ? at + g.aoff[l] + k0 : bt + g.boff[l - A_LD] + k0;
                 if (in)
@@ -161,21 +180,6 @@ __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // the next stage has landed from this wavefront (only the stage just
-    // issued may still be in flight); the barrier makes it complete for all,
-    // and frees this stage's buffer for reuse
-    if (ahead)
-        stage_barrier<(STAGES - 2) * NLD>();
-    else
-        stage_barrier<0>();
-    // with double buffering the next stage is the one just loaded into `wr`
-    // (and `nx` is not accessed), otherwise it is `nx`
-    const uint4 *next = STAGES == 2 ? wr : nx;
-    const int ch0 = half ^ fswz;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) xa[0][i] = __builtin_bit_cast(v4i, next[a_frag + i * 32 * kCPR + ch0]);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) wb[0][j] = __builtin_bit_cast(v4i, next[b_frag + j * 32 * kCPR + ch0]);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool KTAIL, bool OUT_I32>

@@ -1,14 +1,16 @@
-// Dynamic per-row int8 quantization: one wavefront per row.
+// Dynamic per-row int8 quantization.
 //
 //   s = fl32(absmax / 127);  q = clamp(rint(fl32(x / s)), -127, 127)
 //
 // (absmax / 127 scale: Paddle sparse_fc PR #41770, spmm_plugin.cu weight-scale
 // hunk; clamp before the cast: vLLM csrc/quantization log, FP8 clamp commit.)
 //
-// The pass is HBM bound (2 or 4 bytes in, 1 byte out per element): each lane
-// moves 16 input bytes per load, the wave reduces the absmax with cross-lane
-// shuffles, and rows of up to 4096 elements stay in registers so the input is
-// read once.
+// The pass is HBM bound (2 or 4 bytes in, 1 byte out per element). A row is
+// split over WPR wavefronts (several for long rows, so a short batch still
+// fills the chip); every lane moves 16 input bytes per load, the absmax is
+// reduced across lanes with shuffles and across the row's wavefronts through
+// LDS, and rows of up to NCH*64*8*WPR elements stay in registers so the input
+// is read once.
 //
 // Exact division, cheaply. The quantized value must equal rint of the
 // correctly rounded binary32 quotient x / s. Per element we form
@@ -19,42 +21,56 @@
 // IEEE division. Rows whose scale is subnormal (1/s would overflow) always
 // divide. The vLLM log's inverted-scale trick alone would not be exact: it
 // moves about one element per 4096-wide row across a rounding boundary.
+//
+// Rounding and the byte in one add: for |t| < 2^22, m = fl(t + 1.5 * 2^23)
+// rounds t to the nearest integer, ties to even, and the low byte of m's bit
+// pattern is that integer in two's complement. |t| <= 127 here, so the clamp
+// of the definition never binds on this path.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace w8a8 {
 namespace {
 
-constexpr int kRowsPerBlock = 4;  // one row per wave, 4 waves per workgroup
-constexpr int kMaxRegChunks = 8;  // rows up to 8 * 64 * 8 = 4096 elements stay in registers
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kMaxRegChunks = 8;     // chunks of 8 elements held per lane
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr float kTieGuard = 0.5f - 0x1p-14f;
 
-// 8 consecutive inputs -> float (bf16 widening is exact).
-__device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
+// 8 consecutive inputs -> float (bf16 widening is exact), and their absmax
+// folded into `amax` (non-negative floats order like their bit patterns).
+__device__ __forceinline__ void load8(const uint16_t *p, float v[8], uint32_t &amax) {
     const uint4 u = *reinterpret_cast<const uint4 *>(p);
-    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
-    v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
-    v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        v[2 * h] = bf16_lo(w[h]);
+        v[2 * h + 1] = bf16_hi(w[h]);
+        const uint32_t a = w[h] & 0x7FFF7FFFu;
+        const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
+        amax = max(amax, max(lo, hi) << 16);
+    }
 }
 
-__device__ __forceinline__ void load8(const float *p, float v[8]) {
+__device__ __forceinline__ void load8(const float *p, float v[8], uint32_t &amax) {
     const float4 a = reinterpret_cast<const float4 *>(p)[0];
     const float4 b = reinterpret_cast<const float4 *>(p)[1];
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    float m = __uint_as_float(amax);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+    amax = __float_as_uint(m);
 }
 
-__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
-
-// Non-negative floats order like their bit patterns, so the absmax is an
-// unsigned max over the wave.
-__device__ __forceinline__ float wave_absmax(uint32_t bits) {
+__device__ __forceinline__ uint32_t wave_max(uint32_t bits) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const uint32_t o = __shfl_xor(bits, off, kWave);
         bits = bits > o ? bits : o;
     }
-    return __uint_as_float(bits);
+    return bits;
 }
 
 struct RowScale {
@@ -71,87 +87,106 @@ __device__ __forceinline__ RowScale row_scale(float absmax) {
     return rs;
 }
 
-__device__ __forceinline__ int quantize1(float x, const RowScale &rs) {
-    float q;
-    if (rs.fast) {
-        const float t = x * rs.r;
-        const float k = __builtin_rintf(t);
-        q = (__builtin_fabsf(t - k) < 0.5f - 0x1p-14f) ? k : __builtin_rintf(x / rs.s);
-    } else {
-        q = rs.s == 0.0f ? 0.0f : __builtin_rintf(x / rs.s);
-    }
-    q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
-    return (int)q;
+// The byte of rint(fl(x / s)) clamped to [-127, 127], by IEEE division.
+__device__ __forceinline__ uint32_t quantize_div(float x, float s) {
+    if (s == 0.0f) return 0;
+    const float q = __builtin_fminf(__builtin_fmaxf(x / s, -127.0f), 127.0f);
+    return __float_as_uint(q + kMagic) & 0xFFu;
 }
 
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+    return (b0 & 0xFFu) | ((b1 & 0xFFu) << 8) | ((b2 & 0xFFu) << 16) | (b3 << 24);
+}
+
+// 8 values -> 8 int8 codes (two packed words)
 __device__ __forceinline__ uint2 quantize8(const float v[8], const RowScale &rs) {
-    uint32_t w[2];
+    uint32_t b[8];
+    if (rs.fast) {
+        bool near_tie = false;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint32_t b0 = (uint32_t)quantize1(v[4 * h + 0], rs) & 0xFFu;
-        const uint32_t b1 = (uint32_t)quantize1(v[4 * h + 1], rs) & 0xFFu;
-        const uint32_t b2 = (uint32_t)quantize1(v[4 * h + 2], rs) & 0xFFu;
-        const uint32_t b3 = (uint32_t)quantize1(v[4 * h + 3], rs) & 0xFFu;
-        w[h] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        for (int e = 0; e < 8; ++e) {
+            const float t = v[e] * rs.r;
+            const float m = t + kMagic;
+            const float k = m - kMagic;  // rint(t), exact
+            near_tie |= __builtin_fabsf(t - k) >= kTieGuard;
+            b[e] = __float_as_uint(m);
+        }
+        if (near_tie) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[e] = quantize_div(v[e], rs.s);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b[e] = quantize_div(v[e], rs.s);
     }
-    return make_uint2(w[0], w[1]);
+    return make_uint2(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]));
 }
 
-// NCH > 0: the row (at most NCH * 512 elements) is held in registers.
-// NCH == 0: any K; the row is read twice (the second read hits the L2).
-template <typename T, int NCH>
-__global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_kernel(
+// Row m is handled by WPR consecutive wavefronts; wavefront w of the row takes
+// the 8-element chunks w*64 + lane + c*64*WPR (so the row's wavefronts read
+// consecutive kilobytes). NCH > 0: at most NCH chunks per lane, held in
+// registers. NCH == 0: any K, the row is read twice (the second read hits L2).
+template <typename T, int NCH, int WPR>
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
     const T *__restrict__ x, int64_t M, int K, int8_t *__restrict__ xq, float *__restrict__ xs) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
-    if (row >= M) return;  // uniform per wave
-    const T *xr = x + row * K;
-    int8_t *qr = xq + row * K;
+    constexpr int kRowsPerBlock = kWavesPerBlock / WPR;
+    __shared__ uint32_t red[kWavesPerBlock];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int sub = wave % WPR;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + wave / WPR;
+    const bool live = row < M;  // uniform per wavefront
+    const T *xr = x + (live ? row : 0) * K;
+    int8_t *qr = xq + (live ? row : 0) * K;
     const int nch = K >> 3;  // 8-element chunks (K % 16 == 0)
-    uint32_t bits = 0;
+    const int first = sub * kWave + lane, stride = kWave * WPR;
+
+    uint32_t amax = 0;
+    float v[NCH > 0 ? NCH : 1][8];
     if constexpr (NCH > 0) {
-        float v[NCH][8];
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int ch = c * kWave + lane;
-            if (ch < nch) {
-                load8(xr + ch * 8, v[c]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bits = max(bits, abs_bits(v[c][e]));
-            }
+            const int ch = first + c * stride;
+            if (live && ch < nch) load8(xr + ch * 8, v[c], amax);
         }
-        const RowScale rs = row_scale(wave_absmax(bits));
+    } else {
+        for (int ch = first; live && ch < nch; ch += stride) load8(xr + ch * 8, v[0], amax);
+    }
+    amax = wave_max(amax);
+    if constexpr (WPR > 1) {
+        if (lane == 0) red[wave] = amax;
+        __syncthreads();
+        const int base = (wave / WPR) * WPR;
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) amax = max(amax, red[base + w]);
+    }
+    if (!live) return;
+    const RowScale rs = row_scale(__uint_as_float(amax));
+    if constexpr (NCH > 0) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int ch = c * kWave + lane;
+            const int ch = first + c * stride;
             if (ch < nch) *reinterpret_cast<uint2 *>(qr + ch * 8) = quantize8(v[c], rs);
         }
-        if (lane == 0) xs[row] = rs.s;
     } else {
-        for (int ch = lane; ch < nch; ch += kWave) {
-            float v[8];
-            load8(xr + ch * 8, v);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bits = max(bits, abs_bits(v[e]));
+        for (int ch = first; ch < nch; ch += stride) {
+            uint32_t unused = 0;
+            load8(xr + ch * 8, v[0], unused);
+            *reinterpret_cast<uint2 *>(qr + ch * 8) = quantize8(v[0], rs);
         }
-        const RowScale rs = row_scale(wave_absmax(bits));
-        for (int ch = lane; ch < nch; ch += kWave) {
-            float v[8];
-            load8(xr + ch * 8, v);
-            *reinterpret_cast<uint2 *>(qr + ch * 8) = quantize8(v, rs);
-        }
-        if (lane == 0) xs[row] = rs.s;
     }
+    if (sub == 0 && lane == 0) xs[row] = rs.s;
 }
 
-template <typename T>
-hipError_t launch_quantize(const T *x, int64_t M, int K, int8_t *xq, float *xs, hipStream_t stream) {
-    const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
-    const dim3 block(kRowsPerBlock * kWave);
-    const int chunks_per_lane = ((K >> 3) + kWave - 1) / kWave;
+template <typename T, int WPR>
+hipError_t launch_wpr(const T *x, int64_t M, int K, int8_t *xq, float *xs, hipStream_t stream) {
+    constexpr int kRowsPerBlock = kWavesPerBlock / WPR;
+    const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(kThreads);
+    const int chunks_per_lane = ((K >> 3) + kWave * WPR - 1) / (kWave * WPR);
     switch (chunks_per_lane) {
-#define W8A8_Q_CASE(n) \
-    case n: quantize_rows_kernel<T, n><<<grid, block, 0, stream>>>(x, M, K, xq, xs); break;
+#define W8A8_Q_CASE(n)                                                                       \
+    case n:                                                                                  \
+        quantize_rows_kernel<T, n, WPR><<<grid, block, 0, stream>>>(x, M, K, xq, xs);         \
+        break;
         W8A8_Q_CASE(1)
         W8A8_Q_CASE(2)
         W8A8_Q_CASE(3)
@@ -163,9 +198,17 @@ hipError_t launch_quantize(const T *x, int64_t M, int K, int8_t *xq, float *xs, 
 #undef W8A8_Q_CASE
         default:
             static_assert(kMaxRegChunks == 8, "switch covers 1..kMaxRegChunks");
-            quantize_rows_kernel<T, 0><<<grid, block, 0, stream>>>(x, M, K, xq, xs);
+            quantize_rows_kernel<T, 0, WPR><<<grid, block, 0, stream>>>(x, M, K, xq, xs);
     }
     return hipGetLastError();
+}
+
+// Four wavefronts per row while that still leaves at least 8192 wavefronts
+// and each lane 2+ chunks; otherwise one wavefront per row.
+template <typename T>
+hipError_t launch_quantize(const T *x, int64_t M, int K, int8_t *xq, float *xs, hipStream_t stream) {
+    if (M < 8192 && K >= 4 * kWave * 8 * 2) return launch_wpr<T, 4>(x, M, K, xq, xs, stream);
+    return launch_wpr<T, 1>(x, M, K, xq, xs, stream);
 }
 
 }  // namespace
