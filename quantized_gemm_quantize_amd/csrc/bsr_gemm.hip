@@ -27,13 +27,20 @@
 //    the previous block may be refilled;
 //  - the epilogue stages each consumer's rows through a private LDS region,
 //    32 rows x 128 bytes at a time, and stores whole 128-byte lines with
-//    16-byte stores, in the final
-//    [M, N] layout (pytorch/ao PR #821, the two .t().contiguous() removals);
+//    16-byte streaming (nontemporal) stores, in the final [M, N] layout
+//    (pytorch/ao PR #821, the two .t().contiguous() removals); streaming
+//    stores keep the output from evicting X from L2;
 //  - LDS rows are 64 bytes; chunk c of row r sits at slot c ^ ((r / 2) % 4),
 //    so 8 consecutive lanes reading one chunk of 8 consecutive rows touch 8
 //    distinct 16-byte bank groups;
-//  - each XCD owns a contiguous range of tiles (whole X slabs), so the ~8
-//    block rows that read one X block find it in that XCD's L2.
+//  - the workgroups of one XCD walk a contiguous tile range side by side:
+//    the ~8 block rows that read one X block find it in that XCD's L2, and
+//    their stores land in adjacent 128-byte pieces of the same output rows
+//    (scattered 128-byte pieces cost the write path about 10%);
+//  - measured and not kept: 8 consumers of 32 rows each
+//    (more store streams, but more barrier and LDS traffic) and equal-work
+//    contiguous tile runs (better balance, scattered stores).
+#include <numeric>
 #include <type_traits>
 
 #include "common.hpp"
@@ -44,11 +51,14 @@ namespace {
 
 constexpr int kBS = 64;          // block size
 constexpr int kBM = 256;         // rows of X per tile
-constexpr int kMathWaves = 4;    // consumers, 64 rows each
+constexpr int kMathWaves = 4;    // consumers, kRowsPerMath rows each
 constexpr int kLoadWaves = 4;    // producers
 constexpr int kThreads = (kMathWaves + kLoadWaves) * kWave;
 constexpr int kRowSlots = 4;     // 16-byte slots per 64-byte LDS row
 constexpr int kStages = 3;       // ring depth
+constexpr int kRowsPerMath = kBM / kMathWaves;  // 32: one 32-row MFMA tile
+constexpr int kTM = kRowsPerMath / 32;
+static_assert(kTM >= 1 && kRowsPerMath % 32 == 0, "whole 32-row MFMA tiles per consumer");
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
@@ -65,7 +75,8 @@ constexpr int kSaSlots = kBM * 4 / 16;                   // 1 KB
 constexpr int kSbSlots = kBS * 4 / 16;                   // 256 B
 constexpr int kWOff = kXSlots, kSaOff = kWOff + kWSlots, kSbOff = kSaOff + kSaSlots;
 constexpr int kBufSlots = kSbOff + kSbSlots;             // 21.25 KB
-constexpr int kStageSlots = 32 * 8;                      // 4 KB per consumer: 32 rows x 128 B
+constexpr int kSR = kRowsPerMath >= 32 && kMathWaves <= 4 ? 32 : 16;  // staging rows per pass
+constexpr int kStageSlots = kSR * 8;                     // per consumer: kSR rows x 128 B
 constexpr int kLdsSlots = kStages * kBufSlots + kMathWaves * kStageSlots;
 // Tiles are taken in segments of up to kSegTiles, whose stored-block ranges
 // sit in a small LDS table.
@@ -107,17 +118,33 @@ __device__ __forceinline__ int load_index(const int32_t *p, int i) {
     return ((const_i32 *)p)[i];
 }
 
+struct Args {
+    const int8_t *A;
+    const float *sa;
+    const int32_t *crow, *col;
+    const int8_t *values;
+    const float *sb;
+    void *out;
+    int nnzb, M, N, K, block_rows;
+};
+
 // The tiles of one workgroup: lo, lo + step, ... < hi. Tile t is X slab
 // t / block_rows times block row t % block_rows.
 struct TileList {
     int lo, hi, step;
 };
 
+// The tiles of workgroup b: XCD x = b % 8 owns the contiguous tile range
+// [x T / 8, (x + 1) T / 8), and its P / 8 workgroups take every (P / 8)-th
+// tile of it. The workgroups of an XCD thus work on neighbouring tiles at the
+// same time: one X slab in its L2, and output stores to adjacent 128-byte
+// pieces of the same rows. The host makes P / 8 coprime with the block-row
+// count, so each workgroup's tiles cycle through all block rows and the
+// per-workgroup work (stored blocks) evens out.
 __device__ __forceinline__ TileList tile_list(int tiles) {
-    TileList L;
     const int P = (int)gridDim.x, b = (int)blockIdx.x;
+    TileList L;
     if (P >= kXcds && P % kXcds == 0) {
-        // workgroup b runs on XCD b % 8; XCD x owns tiles [x T / 8, (x+1) T / 8)
         const int x = b % kXcds;
         L.lo = (int)((int64_t)tiles * x / kXcds) + b / kXcds;
         L.hi = (int)((int64_t)tiles * (x + 1) / kXcds);
@@ -129,16 +156,6 @@ __device__ __forceinline__ TileList tile_list(int tiles) {
     }
     return L;
 }
-
-struct Args {
-    const int8_t *A;
-    const float *sa;
-    const int32_t *crow, *col;
-    const int8_t *values;
-    const float *sb;
-    void *out;
-    int nnzb, M, N, K, block_rows;
-};
 
 // ---- producers ----------------------------------------------------------
 
@@ -241,11 +258,11 @@ __device__ __forceinline__ void store16(void *p, uint4 v) {
 
 template <typename OutT>
 __device__ __forceinline__ void store_zero_rows(const Args &a, int m0, int br, int w, int lane) {
-    // 64 rows x 64 outputs as 16-byte pieces
+    // kRowsPerMath rows x 64 outputs as 16-byte pieces
     constexpr int kPieces = kBS * (int)sizeof(OutT) / 16;
     constexpr int kPer = 16 / (int)sizeof(OutT);
-    for (int q = lane; q < 64 * kPieces; q += kWave) {
-        const int row = m0 + 64 * w + q / kPieces;
+    for (int q = lane; q < kRowsPerMath * kPieces; q += kWave) {
+        const int row = m0 + kRowsPerMath * w + q / kPieces;
         if (row < a.M)
             store16(static_cast<OutT *>(a.out) + (int64_t)row * a.N + br * kBS + (q % kPieces) * kPer,
                     make_uint4(0, 0, 0, 0));
@@ -253,62 +270,93 @@ __device__ __forceinline__ void store_zero_rows(const Args &a, int m0, int br, i
 }
 
 // Tile (i, jt), element r of a lane: row 32 i + lane % 32 of this consumer's
-// 64, channel 32 jt + 8 (r / 4) + 4 (lane / 32) + r % 4 (the weight is the
-// first MFMA operand). The outputs go out in passes of 32 rows x 128 bytes
+// rows, channel 32 jt + 8 (r / 4) + 4 (lane / 32) + r % 4 (the weight is the
+// first MFMA operand). The outputs go out in passes of kSR rows x 128 bytes
 // (64 bf16 or 32 int32 channels), whole 128-byte lines: scale, write the pass
 // into the private staging rows (16-byte chunk c of row r at slot
 // c ^ oswz(r)), read it back as 16-byte pieces, 8 lanes per row, and store.
 // Half-line (64-byte) pieces cost the write path about half its rate.
 template <typename OutT>
 __device__ __forceinline__ void store_tile(const Args &a, const uint4 *__restrict__ buf,
-                                           uint4 *__restrict__ stg, const v16i (&acc)[2][2], int m0,
-                                           int br, int w, int lane) {
+                                           uint4 *__restrict__ stg, const v16i (&acc)[kTM][2],
+                                           int m0, int br, int w, int lane) {
     constexpr bool kI32 = std::is_same<OutT, int32_t>::value;
     constexpr int kCp = 128 / (int)sizeof(OutT);  // channels per 128-byte row piece
     constexpr int kPieces = kBS / kCp;            // pieces per row: 1 (bf16) or 2 (int32)
     const int frag_row = lane & 31, half = lane >> 5;
+    const int srow = frag_row & (kSR - 1);        // this lane's row within a pass
     const float *sa_l = reinterpret_cast<const float *>(buf + kSaOff);
     const float *sb_l = reinterpret_cast<const float *>(buf + kSbOff);
     char *sbytes = reinterpret_cast<char *>(stg);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const float sx = kI32 ? 0.0f : sa_l[64 * w + 32 * i + frag_row];
+    for (int rg = 0; rg < kRowsPerMath / kSR; ++rg) {
+        const int i = rg * kSR / 32;  // MFMA row tile of this pass
+        // with 16-row passes, half of the lanes hold the pass's rows
+        const bool mine = kSR == 32 || (frag_row >> 4) == (rg & 1);
+        const float sx = kI32 ? 0.0f : sa_l[kRowsPerMath * w + 32 * i + frag_row];
 #pragma unroll
         for (int h = 0; h < kPieces; ++h) {
+            if (mine) {
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-                if ((32 * jt) / kCp != h) continue;
+                for (int jt = 0; jt < 2; ++jt) {
+                    if ((32 * jt) / kCp != h) continue;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int c0 = 32 * jt + 8 * g + 4 * half;               // first of 4 channels
-                    const int off = (c0 - kCp * h) * (int)sizeof(OutT);      // byte in the piece
-                    char *dst = sbytes + frag_row * 128 + (((off >> 4) ^ oswz(frag_row)) << 4) +
-                                (off & 15);
-                    if constexpr (kI32) {
-                        *reinterpret_cast<v4i *>(dst) =
-                            v4i{acc[i][jt][4 * g], acc[i][jt][4 * g + 1], acc[i][jt][4 * g + 2],
-                                acc[i][jt][4 * g + 3]};
-                    } else {
-                        const float4 s = *reinterpret_cast<const float4 *>(sb_l + c0);
-                        const uint32_t lo = pack_bf16x2((float)acc[i][jt][4 * g] * sx * s.x,
-                                                        (float)acc[i][jt][4 * g + 1] * sx * s.y);
-                        const uint32_t hi = pack_bf16x2((float)acc[i][jt][4 * g + 2] * sx * s.z,
-                                                        (float)acc[i][jt][4 * g + 3] * sx * s.w);
-                        *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
+                    for (int g = 0; g < 4; ++g) {
+                        const int c0 = 32 * jt + 8 * g + 4 * half;           // first of 4 channels
+                        const int off = (c0 - kCp * h) * (int)sizeof(OutT);  // byte in the piece
+                        char *dst = sbytes + srow * 128 + (((off >> 4) ^ oswz(srow)) << 4) + (off & 15);
+                        if constexpr (kI32) {
+                            *reinterpret_cast<v4i *>(dst) =
+                                v4i{acc[i][jt][4 * g], acc[i][jt][4 * g + 1], acc[i][jt][4 * g + 2],
+                                    acc[i][jt][4 * g + 3]};
+                        } else {
+                            const float4 s = *reinterpret_cast<const float4 *>(sb_l + c0);
+                            const uint32_t lo = pack_bf16x2((float)acc[i][jt][4 * g] * sx * s.x,
+                                                            (float)acc[i][jt][4 * g + 1] * sx * s.y);
+                            const uint32_t hi = pack_bf16x2((float)acc[i][jt][4 * g + 2] * sx * s.z,
+                                                            (float)acc[i][jt][4 * g + 3] * sx * s.w);
+                            *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
+                        }
                     }
                 }
             }
 #pragma unroll
-            for (int r8 = 0; r8 < 4; ++r8) {
+            for (int r8 = 0; r8 < kSR / 8; ++r8) {
                 const int rr = 8 * r8 + (lane >> 3), lc = lane & 7;
                 const uint4 v = stg[rr * 8 + (lc ^ oswz(rr))];
-                const int row = m0 + 64 * w + 32 * i + rr;
+                const int row = m0 + kRowsPerMath * w + rg * kSR + rr;
                 if (row < a.M)
                     store16(static_cast<OutT *>(a.out) + (int64_t)row * a.N + br * kBS + kCp * h +
                                 lc * (16 / (int)sizeof(OutT)),
                             v);
             }
         }
+    }
+}
+
+// One stored block for a consumer: its rows of X times the weight block,
+// two K=32 steps of kTM x 2 MFMA tiles; FIRST starts from zero.
+template <bool FIRST>
+__device__ __forceinline__ void multiply_block(const uint4 *buf, int w, int frag_row, int half,
+                                               v16i (&acc)[kTM][2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        v4i xa[kTM], wb[2];
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) {
+            const int r = kRowsPerMath * w + 32 * i + frag_row;
+            xa[i] = __builtin_bit_cast(v4i, buf[r * kRowSlots + ((kk * 2 + half) ^ bswz(r))]);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+            const int r = 32 * jt + frag_row;
+            wb[jt] = __builtin_bit_cast(v4i, buf[kWOff + r * kRowSlots + ((kk * 2 + half) ^ bswz(r))]);
+        }
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+                acc[i][jt] = mfma_32x32x32(wb[jt], xa[i], FIRST && kk == 0 ? v16i{} : acc[i][jt]);
     }
 }
 
@@ -329,35 +377,17 @@ __device__ __forceinline__ void consumer(const Args &a, uint4 *lds, const int2 *
             store_zero_rows<OutT>(a, m0, br, w, lane);
             continue;
         }
-        v16i acc[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt) acc[i][jt] = v16i{};
-        const uint4 *buf = lds;
-        for (int j = j0; j < j1; ++j, ++n) {
+        // the first block starts the accumulators from zero (an inline
+        // constant operand of the MFMA, no register clearing)
+        v16i acc[kTM][2];
+        lds_barrier();
+        const uint4 *buf = lds + (n % kStages) * kBufSlots;
+        multiply_block<true>(buf, w, frag_row, half, acc);
+        ++n;
+        for (int j = j0 + 1; j < j1; ++j, ++n) {
             lds_barrier();
             buf = lds + (n % kStages) * kBufSlots;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                v4i xa[2], wb[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int r = 64 * w + 32 * i + frag_row;
-                    xa[i] = __builtin_bit_cast(v4i, buf[r * kRowSlots + ((kk * 2 + half) ^ bswz(r))]);
-                }
-#pragma unroll
-                for (int jt = 0; jt < 2; ++jt) {
-                    const int r = 32 * jt + frag_row;
-                    wb[jt] = __builtin_bit_cast(
-                        v4i, buf[kWOff + r * kRowSlots + ((kk * 2 + half) ^ bswz(r))]);
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int jt = 0; jt < 2; ++jt)
-                        acc[i][jt] = mfma_32x32x32(wb[jt], xa[i], acc[i][jt]);
-            }
+            multiply_block<false>(buf, w, frag_row, half, acc);
         }
         // the buffer of the tile's last block (with its scales) is refilled
         // only after the next barrier, which this wavefront reaches after
@@ -367,7 +397,7 @@ __device__ __forceinline__ void consumer(const Args &a, uint4 *lds, const int2 *
 }
 
 template <bool OUT_I32>
-__global__ __launch_bounds__(kThreads) void bsr_gemm_kernel(Args a, int tiles) {
+__global__ __launch_bounds__(kThreads) void bsr_gemm_kernel(Args a, int slabs) {
     using OutT = typename std::conditional<OUT_I32, int32_t, __bf16>::type;
     __shared__ uint4 lds[kLdsSlots];
     __shared__ int2 meta[kSegTiles];  // stored-block range of each tile of the segment
@@ -376,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void bsr_gemm_kernel(Args a, int tiles) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const bool math = wave < kMathWaves;
-    const TileList L = tile_list(tiles);
+    const TileList L = tile_list(slabs * a.block_rows);
     const int nt = list_len(L);
     // The roles branch once, each with its own segment loop, so that the
     // compiler's wait analysis of the consumers never sees the producers'
@@ -435,12 +465,19 @@ hipError_t launch_bsr_gemm(const int8_t *xq, const float *xs, int M, int K, cons
     int P = 2 * device_cus();
     if (P > tiles) P = tiles;
     if (P >= kXcds) P -= P % kXcds;
+    if (P >= kXcds) {
+        // a stride coprime with the block-row count walks each workgroup
+        // through all block rows
+        int per = P / kXcds;
+        while (per > 1 && std::gcd(per, block_rows) != 1) --per;
+        P = per * kXcds;
+    }
     const Args a{xq, xs, crow, col, values, ws, out, nnzb, M, N, K, block_rows};
     const dim3 grid((unsigned)P), block(kThreads);
     if (out_i32)
-        bsr_gemm_kernel<true><<<grid, block, 0, stream>>>(a, tiles);
+        bsr_gemm_kernel<true><<<grid, block, 0, stream>>>(a, slabs);
     else
-        bsr_gemm_kernel<false><<<grid, block, 0, stream>>>(a, tiles);
+        bsr_gemm_kernel<false><<<grid, block, 0, stream>>>(a, slabs);
     return hipGetLastError();
 }
 

@@ -257,7 +257,7 @@ def _bsr_case(b, oracle, M, N, K, zero_frac, seed, rows=None):
 
 @pytest.mark.parametrize("M,N,K,zf", [(1, 64, 64, 0.0), (16, 128, 128, 0.5), (129, 256, 192, 0.7),
                                       (300, 512, 320, 0.9), (200, 192, 128, 1.0),
-                                      (64, 320, 256, 0.0)])
+                                      (64, 320, 256, 0.0), (64, 4480, 5120, 0.0)])
 def test_bsr_shapes(b, oracle, M, N, K, zf):
     log(f"bsr M={M} N={N} K={K} zero_frac={zf}")
     _bsr_case(b, oracle, M, N, K, zf, seed=M + N + K)
@@ -270,6 +270,16 @@ def test_bsr_workload_full_size(b, oracle):
     worst, n_empty = _bsr_case(b, oracle, cfg["M"], cfg["N"], cfg["K"], cfg["zero_frac"], seed=0,
                                rows=inp_rows)
     log(f"  bsr: {len(inp_rows)} rows compared, max {worst} ulp, {n_empty} empty block rows")
+
+
+def test_bsr_many_tiles_per_workgroup(b, oracle):
+    """16640 output tiles (65 row slabs x 256 block rows): each persistent
+    workgroup runs through more than one segment of its tile table."""
+    M, N, K = 16448, 16384, 128
+    log(f"bsr many tiles M={M} N={N} K={K}")
+    rows = _sampled_rows(M)
+    worst, n_empty = _bsr_case(b, oracle, M, N, K, 0.9, seed=5, rows=rows)
+    log(f"  {len(rows)} rows compared, max {worst} ulp, {n_empty} empty block rows")
 
 
 def test_bsr_matches_dense_gemm(b, oracle):
