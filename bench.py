@@ -51,6 +51,12 @@ def parse():
                     choices=["tiny", "decode", "prefill_outliers", "large_m", "bsr"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every timed call directly instead of replaying HIP graphs "
+                         "(for profilers that count per dispatch)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy five times (the "
+                         "reference for scaling HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -67,7 +73,7 @@ def rotation(bytes_per_set: int) -> int:
     return max(2, -(-2 * MALL_BYTES // max(bytes_per_set, 1)) + 1)
 
 
-def time_loop(fn, n: int, torch, period: int = 1) -> float:
+def time_loop(fn, n: int, torch, period: int = 1, eager: bool = False) -> float:
     """Average ms per call of fn(i) over exactly n calls, replayed from HIP graphs.
 
     The calls are captured into a graph of `period` consecutive calls (one per
@@ -75,8 +81,20 @@ def time_loop(fn, n: int, torch, period: int = 1) -> float:
     holds exactly n calls and the GPU runs them back to back without waiting on
     Python (an eager call costs several microseconds of host time). HIP events
     bracket the replays on the stream they run on; the region is bracketed by
-    device synchronization on both sides.
+    device synchronization on both sides. With eager=True the n calls are
+    launched directly (host launch overhead included).
     """
+    if eager:
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(n):
+            fn(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / n
+
     def capture(count):
         if count == 0:
             return None
@@ -143,7 +161,7 @@ def cpu_baseline(name: str, np):
                       f"quantize + exact int GEMM + float64 epilogue, {t:.2f} s wall"}
 
 
-def bench_decode(torch, np, b, dev, steps, warmup):
+def bench_decode(torch, np, b, dev, steps, warmup, eager=False):
     """M=16 weight-streaming GEMM: GB/s with weight copies rotated past the Infinity Cache."""
     d = prepare("decode", torch, np, b, dev)
     M, N, K = d["inp"].M, d["inp"].N, d["inp"].K
@@ -160,8 +178,8 @@ def bench_decode(torch, np, b, dev, steps, warmup):
 
     for i in range(warmup):
         step(i)
-    ms_gemm = time_loop(gemm, steps, torch, period=R)
-    ms_step = time_loop(step, steps, torch, period=R)
+    ms_gemm = time_loop(gemm, steps, torch, period=R, eager=eager)
+    ms_step = time_loop(step, steps, torch, period=R, eager=eager)
     gemm_bytes = M * K + 4 * M + N * K + 4 * N + 2 * M * N
     layer_bytes = 2 * M * K + N * K + 4 * N + 2 * M * N
     gbs = gemm_bytes / (ms_gemm * 1e-3) / 1e9
@@ -181,6 +199,16 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        nbytes = 256 << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 5}), flush=True)
+        return
 
     from quantized_gemm_quantize_amd import binding as b
     b.load()
@@ -222,12 +250,12 @@ def main():
         step(i)
     torch.cuda.synchronize()
     eager_out = outs[0].clone()
-    ms_step = time_loop(step, args.steps, torch, period=R)
+    ms_step = time_loop(step, args.steps, torch, period=R, eager=args.eager)
     # graph replays recompute the same outputs: check the first set bit for bit
     if not torch.equal(outs[0].view(torch.int16), eager_out.view(torch.int16)):
         raise RuntimeError("graph replay output differs from the eager output")
-    ms_gemm = time_loop(gemm, args.steps, torch, period=R)
-    ms_quant = time_loop(quant, args.steps, torch, period=R)
+    ms_gemm = time_loop(gemm, args.steps, torch, period=R, eager=args.eager)
+    ms_quant = time_loop(quant, args.steps, torch, period=R, eager=args.eager)
 
     ops = 2.0 * M * N * K
     if bsr:
@@ -268,6 +296,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
+        "timing": "eager launches" if args.eager else "HIP graph replay",
         "config": {"workload": f"{name} M={M} K={K} N={N}" + (f" BSR 64x64 nnzb={d['values'].shape[0]}" if bsr else ""),
                    "step": "w8a8_quantize_rows + " + ("w8a8_bsr_gemm" if bsr else "w8a8_gemm"),
                    "seed": 0, "input_sets_rotated": R},
@@ -279,7 +308,7 @@ def main():
                       "frac_of_int8_peak": round(gemm_tops / PEAK_INT8_TOPS, 4)},
     }
     if not args.no_decode and name == "prefill_outliers":
-        line["decode_m16"] = bench_decode(torch, np, b, dev, args.steps, args.warmup)
+        line["decode_m16"] = bench_decode(torch, np, b, dev, args.steps, args.warmup, args.eager)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(name, np)
     print(json.dumps(line), flush=True)

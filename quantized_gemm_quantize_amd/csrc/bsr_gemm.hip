@@ -87,28 +87,6 @@ static_assert(kLdsSlots * 16 + kSegTiles * 8 <= 80 * 1024, "two workgroups per C
 // the row scales; producer 0 also loads the channel scales.
 constexpr int kLoads = 6;
 
-// This wavefront's loads up to the last N are in LDS and its LDS accesses are
-// done, then all wavefronts meet. No memory fence: a release fence would also
-// wait for the loads still in flight for later blocks. The empty asm
-// statements keep the compiler from moving memory accesses across.
-template <int N>
-__device__ __forceinline__ void ring_barrier() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier for the consumers: their own LDS accesses are done. They
-// have no loads in flight, and their stores are left to drain.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // The index arrays are read-only here: reading them through the constant
 // address space lets the (uniform) reads be scalar loads, which count on the
 // scalar counter instead of the vector-memory counter the producers' waits
@@ -189,11 +167,11 @@ __device__ __forceinline__ void produce_block(const Args &a, uint4 *buf, int p, 
 __device__ __forceinline__ void producer_barrier(int ahead, bool p0) {
     static_assert(kStages == 3, "the waits below cover ahead in {0, 1}");
     if (ahead <= 0)
-        ring_barrier<0>();
+        vm_barrier<0>();
     else if (p0)
-        ring_barrier<kLoads + 1>();
+        vm_barrier<kLoads + 1>();
     else
-        ring_barrier<kLoads>();
+        vm_barrier<kLoads>();
 }
 
 // Number of tiles in a workgroup's list.
@@ -246,15 +224,6 @@ __device__ __forceinline__ void producer(const Args &a, uint4 *lds, const int2 *
 
 // ---- consumers ----------------------------------------------------------
 
-constexpr bool kStreamStores = true;
-
-// 16-byte output store
-__device__ __forceinline__ void store16(void *p, uint4 v) {
-    if constexpr (kStreamStores)
-        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), reinterpret_cast<v4i *>(p));
-    else
-        *reinterpret_cast<uint4 *>(p) = v;
-}
 
 template <typename OutT>
 __device__ __forceinline__ void store_zero_rows(const Args &a, int m0, int br, int w, int lane) {
@@ -264,7 +233,7 @@ __device__ __forceinline__ void store_zero_rows(const Args &a, int m0, int br, i
     for (int q = lane; q < kRowsPerMath * kPieces; q += kWave) {
         const int row = m0 + kRowsPerMath * w + q / kPieces;
         if (row < a.M)
-            store16(static_cast<OutT *>(a.out) + (int64_t)row * a.N + br * kBS + (q % kPieces) * kPer,
+            store16_nt(static_cast<OutT *>(a.out) + (int64_t)row * a.N + br * kBS + (q % kPieces) * kPer,
                     make_uint4(0, 0, 0, 0));
     }
 }
@@ -326,7 +295,7 @@ __device__ __forceinline__ void store_tile(const Args &a, const uint4 *__restric
                 const uint4 v = stg[rr * 8 + (lc ^ oswz(rr))];
                 const int row = m0 + kRowsPerMath * w + rg * kSR + rr;
                 if (row < a.M)
-                    store16(static_cast<OutT *>(a.out) + (int64_t)row * a.N + br * kBS + kCp * h +
+                    store16_nt(static_cast<OutT *>(a.out) + (int64_t)row * a.N + br * kBS + kCp * h +
                                 lc * (16 / (int)sizeof(OutT)),
                             v);
             }
@@ -423,13 +392,13 @@ __global__ __launch_bounds__(kThreads) void bsr_gemm_kernel(Args a, int slabs) {
     } else {
         for (int s0 = 0; s0 < nt; s0 += kSegTiles) {
             const int cnt = min(kSegTiles, nt - s0);
-            ring_barrier<0>();  // the last segment's loads have all been waited for
+            vm_barrier<0>();  // the last segment's loads have all been waited for
             if (wave == kMathWaves && lane < cnt) {
                 const int br = (L.lo + (s0 + lane) * L.step) % a.block_rows;
                 const int j0 = max(0, min(a.crow[br], a.nnzb));
                 meta[lane] = make_int2(j0, max(j0, min(a.crow[br + 1], a.nnzb)));
             }
-            ring_barrier<0>();
+            vm_barrier<0>();
             producer(a, lds, meta, L, s0, cnt, wave - kMathWaves, lane);
         }
         // nothing is in flight here; saying so keeps the compiler from
@@ -437,21 +406,6 @@ __global__ __launch_bounds__(kThreads) void bsr_gemm_kernel(Args a, int slabs) {
         // two join
         __builtin_amdgcn_s_waitcnt(0);
     }
-}
-
-// CU count of the current device (cached per device)
-int device_cus() {
-    static int cus[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cus[dev] = n;
-    }
-    return cus[dev];
 }
 
 }  // namespace
@@ -462,7 +416,7 @@ hipError_t launch_bsr_gemm(const int8_t *xq, const float *xs, int M, int K, cons
     const int slabs = (M + kBM - 1) / kBM, block_rows = N / kBS;
     const int tiles = slabs * block_rows;
     // two resident workgroups per CU, a multiple of the XCD count
-    int P = 2 * device_cus();
+    int P = 2 * device_cu_count();
     if (P > tiles) P = tiles;
     if (P >= kXcds) P -= P % kXcds;
     if (P >= kXcds) {

@@ -48,4 +48,33 @@ __device__ __forceinline__ int xcd_contiguous(int pid, int tiles) {
     return base + idx;
 }
 
+// Workgroup barrier without a memory fence, for kernels whose loads go
+// straight to LDS: this wavefront's vector-memory operations up to the last N
+// have completed and its LDS operations are done, then all wavefronts meet.
+// (A release fence would wait for every load in flight, including those of
+// later pipeline stages.) The empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that waits for this wavefront's LDS operations only
+// (lgkmcnt(0)); outstanding vector-memory stores are left to drain.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// 16-byte streaming (nontemporal) store.
+__device__ __forceinline__ void store16_nt(void *p, uint4 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), reinterpret_cast<v4i *>(p));
+}
+
 }  // namespace w8a8

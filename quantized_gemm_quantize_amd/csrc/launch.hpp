@@ -17,6 +17,9 @@ hipError_t launch_quantize_rows_f32(const float *x, int64_t M, int K, int8_t *xq
 hipError_t launch_gemm(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
                        int N, int K, void *out, bool out_i32, hipStream_t stream);
 
+// Compute units of the current device (queried once per device).
+int device_cu_count();
+
 hipError_t launch_bsr_gemm(const int8_t *xq, const float *xs, int M, int K, const int32_t *crow,
                            const int32_t *col, const int8_t *values, int nnzb, const float *ws,
                            int N, void *out, bool out_i32, hipStream_t stream);

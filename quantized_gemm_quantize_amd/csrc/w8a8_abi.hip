@@ -51,6 +51,24 @@ w8a8_status quantize_entry(const T *x, int64_t M, int64_t K, int8_t *xq, float *
 
 }  // namespace
 
+namespace w8a8 {
+
+int device_cu_count() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+}  // namespace w8a8
+
 extern "C" {
 
 w8a8_status w8a8_quantize_rows(const void *x_bf16, int64_t M, int64_t K, int8_t *xq,
