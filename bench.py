@@ -20,7 +20,11 @@ The line also carries:
 Inputs are resident in HBM before the timed region; input sets are rotated
 (copies at distinct addresses, more than twice the Infinity Cache in total).
 Launches are captured into HIP graphs and replayed, so the timing is the GPU's
-and not the Python binding's per-call host overhead.
+and not the Python binding's per-call host overhead. ms_per_step is one timed
+region of exactly --steps steps; the kernel-alone figures (gemm_only, the
+roofline's avg_launch_us, quantize_rows) are the median of five regions of
+--steps calls each. Other workloads: --config (the roofline is HBM-bound for
+the BSR kernel and for M <= 64).
 """
 from __future__ import annotations
 
@@ -45,8 +49,8 @@ GEMM_SOURCES = ["gemm_tiled.hip", "common.hpp"]
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="prefill_outliers",
                     choices=["tiny", "decode", "prefill_outliers", "large_m", "bsr"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -69,8 +73,9 @@ def source_hash(names):
 
 
 def rotation(bytes_per_set: int) -> int:
-    """Copies needed for the rotated sets to exceed twice the Infinity Cache."""
-    return max(2, -(-2 * MALL_BYTES // max(bytes_per_set, 1)) + 1)
+    """Copies needed for the rotated sets to exceed twice the Infinity Cache (at most 256:
+    sets of a few kilobytes cannot leave the caches anyway)."""
+    return min(256, max(2, -(-2 * MALL_BYTES // max(bytes_per_set, 1)) + 1))
 
 
 def time_loop(fn, n: int, torch, period: int = 1, eager: bool = False) -> float:
@@ -115,6 +120,13 @@ def time_loop(fn, n: int, torch, period: int = 1, eager: bool = False) -> float:
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / n
+
+
+def time_median(fn, n: int, torch, period: int, eager: bool, repeats: int = 5) -> float:
+    """Median over `repeats` timed regions of time_loop (each of exactly n calls): a single
+    region of a few milliseconds catches the GPU's clock changes."""
+    runs = sorted(time_loop(fn, n, torch, period=period, eager=eager) for _ in range(repeats))
+    return runs[len(runs) // 2]
 
 
 def prepare(name: str, torch, np, b, dev):
@@ -178,8 +190,8 @@ def bench_decode(torch, np, b, dev, steps, warmup, eager=False):
 
     for i in range(warmup):
         step(i)
-    ms_gemm = time_loop(gemm, steps, torch, period=R, eager=eager)
-    ms_step = time_loop(step, steps, torch, period=R, eager=eager)
+    ms_gemm = time_median(gemm, steps, torch, R, eager)
+    ms_step = time_median(step, steps, torch, R, eager)
     gemm_bytes = M * K + 4 * M + N * K + 4 * N + 2 * M * N
     layer_bytes = 2 * M * K + N * K + 4 * N + 2 * M * N
     gbs = gemm_bytes / (ms_gemm * 1e-3) / 1e9
@@ -254,8 +266,9 @@ def main():
     # graph replays recompute the same outputs: check the first set bit for bit
     if not torch.equal(outs[0].view(torch.int16), eager_out.view(torch.int16)):
         raise RuntimeError("graph replay output differs from the eager output")
-    ms_gemm = time_loop(gemm, args.steps, torch, period=R, eager=args.eager)
-    ms_quant = time_loop(quant, args.steps, torch, period=R, eager=args.eager)
+    # the kernels alone: median of 5 regions of K calls each
+    ms_gemm = time_median(gemm, args.steps, torch, R, args.eager)
+    ms_quant = time_median(quant, args.steps, torch, R, args.eager)
 
     ops = 2.0 * M * N * K
     if bsr:
@@ -271,8 +284,10 @@ def main():
         if rec.get("source_hash") == source_hash(GEMM_SOURCES):
             traffic = rec.get("bytes_per_launch")
 
-    if bsr:
-        gemm_bytes = M * K + 4 * M + d["values"].numel() + 4 * N + 2 * M * N
+    if bsr or M <= 64:
+        # HBM bound: the BSR output write, or the M <= 64 weight stream
+        w_bytes = d["values"].numel() if bsr else N * K
+        gemm_bytes = M * K + 4 * M + w_bytes + 4 * N + 2 * M * N
         roof = {"bound": "hbm", "achieved": round(gemm_bytes / (ms_gemm * 1e-3) / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
         roof["frac"] = round(roof["achieved"] / PEAK_HBM_GBS, 4)
