@@ -29,8 +29,9 @@
 //    ends with 4 consecutive output channels of one row: the epilogue scales
 //    them, packs 4 bf16 into 8 bytes and stages the tile in LDS, from where
 //    every store is a full 16-byte piece of a contiguous output row;
-//  - tiles are assigned XCD-contiguously, then in groups of 8 tile rows, so
-//    concurrently running tiles share A and B rows in the same L2.
+//  - tiles are assigned XCD-contiguously, then in groups of 4 (256x128 tiles)
+//    or 8 (256x256) tile rows, so concurrently running tiles share A and B
+//    rows in the same L2.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -41,7 +42,11 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kBK = 128;          // K bytes per stage
 constexpr int kCPR = kBK / 16;    // 16-byte chunks per tile row
-constexpr int kGroupM = 8;
+// tile rows per group in the tile order (see the kernel): 4 for 256x128 tiles
+// (an XCD's 32 tiles then span 1024 rows x 1024 columns: less of A and B per
+// L2), 8 for 256x256
+template <int BN>
+constexpr int group_m() { return BN == 128 ? 4 : 8; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
@@ -114,11 +119,12 @@ __device__ __forceinline__ void load_stage(const int8_t *__restrict__ at, const 
 // may be refilled, and the next stage's first fragments are read while the
 // last K step multiplies instead of after a barrier with nothing to overlap.
 //
-// Per K step kk: TM*TN MFMA slots, each followed by one memory instruction --
-// the fragment reads for the next step first, then this step's share of the
-// direct-to-LDS loads (steps 0-2). The order is pinned with scheduling
-// barriers: a wavefront issues in order, and a burst of loads or reads would
-// hold the MFMAs.
+// Per K step kk: TM*TN MFMA slots. The fragment reads for the next step go
+// out in two bursts, after the first and the second MFMA (reads r with
+// r % 2 == slot), so they have the rest of the step's MFMAs to land; then
+// one direct-to-LDS load follows each further MFMA (this step's share of the
+// stage loads, steps 0-2). The order is pinned with scheduling barriers: a
+// wavefront issues in order, and a burst of loads would hold the MFMAs.
 template <int BM, int TM, int TN, int STAGES, int A_LD, int B_LD, bool KTAIL>
 __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
                                                const int8_t *__restrict__ bt,
@@ -162,14 +168,18 @@ __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
                 acc[i][j] = mfma_32x32x32(wb[f][j], xa[f][i], acc[i][j]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (q < NRD) {
-                if (q < TM)
-                    xa[f ^ 1][q] = __builtin_bit_cast(v4i, src_buf[a_frag + q * 32 * kCPR + ch]);
-                else
-                    wb[f ^ 1][q - TM] = __builtin_bit_cast(v4i, src_buf[b_frag + (q - TM) * 32 * kCPR + ch]);
+            if (q < 2) {
+#pragma unroll
+                for (int r = 0; r < NRD; ++r) {
+                    if (r % 2 != q) continue;
+                    if (r < TM)
+                        xa[f ^ 1][r] = __builtin_bit_cast(v4i, src_buf[a_frag + r * 32 * kCPR + ch]);
+                    else
+                        wb[f ^ 1][r - TM] = __builtin_bit_cast(v4i, src_buf[b_frag + (r - TM) * 32 * kCPR + ch]);
+                }
             }
-            const int l = kk * LPK + (q - NRD);
-            if (kk + 1 < KS && q >= NRD && q < NRD + LPK && l < NLD && ahead) {
+            const int l = kk * LPK + (q - 2);
+            if (kk + 1 < KS && q >= 2 && q < 2 + LPK && l < NLD && ahead) {
                 uint4 *dst = wr + g.wslot + (l < A_LD ? 256 * l : BM * kCPR + 256 * (l - A_LD));
                 const int8_t *src = l < A_LD ? at + g.aoff[l] + k0 : bt + g.boff[l - A_LD] + k0;
                 if (in)
@@ -204,6 +214,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
     // tile coordinates
     const int tiles = tiles_m * tiles_n;
     const int t = xcd_contiguous(blockIdx.x, tiles);
+    constexpr int kGroupM = group_m<BN>();
     const int per_group = kGroupM * tiles_n;
     const int first_m = (t / per_group) * kGroupM;
     const int gsize = min(tiles_m - first_m, kGroupM);
