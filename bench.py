@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="prefill_outliers",
-                    choices=["tiny", "decode", "prefill_outliers", "large_m", "bsr"])
+                    choices=["tiny", "decode", "prefill_outliers", "large_m", "bsr", "bsr_fc2"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--eager", action="store_true",

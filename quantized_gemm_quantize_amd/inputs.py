@@ -15,6 +15,9 @@ Workloads (shapes of the pages' examples):
   bsr               X [16448,1280] (64 images x 257 tokens), W [5120,1280] as
                     64x64 blocks with 90% of the blocks zero (ViT-H MLP fc1 shape
                     from the bsr_dense_addmm warning in pytorch/ao PR #821)
+  bsr_fc2           X [16448,5120], W [1280,5120] as 64x64 blocks with 80% of the
+                    blocks zero (the ViT-H MLP fc2 shape of the same warning, at
+                    the 0.8 linear sparsity of that benchmark command)
 
 Draw order from numpy.random.default_rng(seed) (PCG64): X ~ N(0,1) float32,
 then the outlier channels, then W = 0.02 * N(0,1) float32, then the block mask.
@@ -32,10 +35,11 @@ CONFIGS = {
     "prefill_outliers": dict(M=2048, K=4096, N=4096, outlier_frac=0.01, outlier_scale=20.0),
     "large_m": dict(M=38400, K=1024, N=4096),
     "bsr": dict(M=16448, K=1280, N=5120, bs=64, zero_frac=0.9),
+    "bsr_fc2": dict(M=16448, K=5120, N=1280, bs=64, zero_frac=0.8),
 }
 
 # Order of the configurations as the workload list states them.
-CONFIG_ORDER = ["tiny", "decode", "prefill_outliers", "large_m", "bsr"]
+CONFIG_ORDER = ["tiny", "decode", "prefill_outliers", "large_m", "bsr", "bsr_fc2"]
 
 
 @dataclass

@@ -263,8 +263,9 @@ def test_bsr_shapes(b, oracle, M, N, K, zf):
     _bsr_case(b, oracle, M, N, K, zf, seed=M + N + K)
 
 
-def test_bsr_workload_full_size(b, oracle):
-    cfg = CONFIGS["bsr"]
+@pytest.mark.parametrize("name", ["bsr", "bsr_fc2"])
+def test_bsr_workload_full_size(b, oracle, name):
+    cfg = CONFIGS[name]
     log(f"bsr workload {cfg}")
     inp_rows = _sampled_rows(cfg["M"])
     worst, n_empty = _bsr_case(b, oracle, cfg["M"], cfg["N"], cfg["K"], cfg["zero_frac"], seed=0,
