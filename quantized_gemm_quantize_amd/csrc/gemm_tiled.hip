@@ -28,7 +28,9 @@
 //  - the MFMA takes the weight fragment as its first operand, so each lane
 //    ends with 4 consecutive output channels of one row: the epilogue scales
 //    them, packs 4 bf16 into 8 bytes and stages the tile in LDS, from where
-//    every store is a full 16-byte piece of a contiguous output row;
+//    every store is a full 16-byte piece of a contiguous output row, written
+//    as a streaming (nontemporal) store so the output does not evict the
+//    operands from L2;
 //  - tiles are assigned XCD-contiguously, then in groups of 4 (256x128 tiles)
 //    or 8 (256x256) tile rows, so concurrently running tiles share A and B
 //    rows in the same L2.
@@ -306,9 +308,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
                 for (int g = 0; g < 4; ++g) {
                     const int n = nw0 + j * 32 + 8 * g + 4 * half;
                     if (n < N)
-                        *reinterpret_cast<v4i *>(static_cast<int32_t *>(out) + (int64_t)m * N + n) =
+                        __builtin_nontemporal_store(
                             v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                acc[i][j][4 * g + 3]};
+                                acc[i][j][4 * g + 3]},
+                            reinterpret_cast<v4i *>(static_cast<int32_t *>(out) + (int64_t)m * N + n));
                 }
         }
     } else {
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
             const int m = mw0 + ml, n = nw0 + cc * 8;
             const uint4 v = st16[ml * CH + (cc ^ (ml & 7))];
             if (m < M && n < N)
-                *reinterpret_cast<uint4 *>(static_cast<__bf16 *>(out) + (int64_t)m * N + n) = v;
+                store16_nt(static_cast<__bf16 *>(out) + (int64_t)m * N + n, v);
         }
     }
 }
