@@ -50,6 +50,9 @@ def load_oracle():
     lib.oracle_bf16_rne_from_f64.restype = ctypes.c_uint16
     lib.oracle_epilogue_bf16.argtypes = [p, p, p, i64, i64, p]
     lib.oracle_epilogue_bf16.restype = None
+    lib.oracle_epilogue_addmm_bf16.argtypes = [p, p, p, p, ctypes.c_double, ctypes.c_double, i64,
+                                                i64, p]
+    lib.oracle_epilogue_addmm_bf16.restype = None
     lib.oracle_bsr_gemm_i32.argtypes = [p, i64, i64, p, p, p, i64, i64, p]
     lib.oracle_bsr_gemm_i32.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
@@ -119,6 +122,26 @@ def epilogue_bf16(acc: np.ndarray, sx: np.ndarray, sw: np.ndarray) -> np.ndarray
         raise ValueError("scale shapes")
     out = np.empty((M, N), np.uint16)
     load_oracle().oracle_epilogue_bf16(_ptr(acc), _ptr(sx), _ptr(sw), M, N, _ptr(out))
+    return out
+
+
+def epilogue_addmm_bf16(acc: np.ndarray, sx: np.ndarray, sw: np.ndarray, bias, alpha: float,
+                        beta: float) -> np.ndarray:
+    """out bf16 bits [M,N] = bf16_rne(alpha * acc * sx[m] * sw[n] + beta * bias[n]), float64;
+    bias None means no bias term."""
+    acc = _c(acc, np.int32)
+    sx = _c(sx, np.float32)
+    sw = _c(sw, np.float32)
+    M, N = acc.shape
+    if sx.shape != (M,) or sw.shape != (N,):
+        raise ValueError("scale shapes")
+    b = None if bias is None else _c(bias, np.float32)
+    if b is not None and b.shape != (N,):
+        raise ValueError("bias shape")
+    out = np.empty((M, N), np.uint16)
+    load_oracle().oracle_epilogue_addmm_bf16(_ptr(acc), _ptr(sx), _ptr(sw),
+                                             None if b is None else _ptr(b), float(alpha),
+                                             float(beta), M, N, _ptr(out))
     return out
 
 

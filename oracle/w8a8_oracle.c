@@ -32,6 +32,12 @@
  *   epilogue:    out[m,n] = bf16_rne(acc * sx[m] * sw[n]) in float64, rounded
  *                once from float64 to bf16 -- "i8i8 -> bf16 matmul to
  *                maintain accuracy", pytorch/ao PR #821, Changes list.
+ *   addmm epilogue: out[m,n] = bf16_rne(alpha * (acc * sx[m] * sw[n])
+ *                + beta * bias[n]) in float64, one rounding to bf16 -- the
+ *                beta / alpha of bsr_dense_addmm (pytorch/ao PR #821, the
+ *                warning's "beta=0 alpha=1"), with the bias a per-channel
+ *                vector as in a linear layer (the pages are silent on its
+ *                shape; plainest reading).
  *   BSR:         the same sum taken only over the stored 64x64 blocks
  *                (crow_indices / col_indices / values), pytorch/ao PR #821
  *                custom-op paragraph and the bsr_dense_addmm warning (Ms=64,
@@ -146,6 +152,26 @@ void oracle_epilogue_bf16(const int32_t *acc, const float *sx, const float *sw, 
         for (int64_t n = 0; n < N; ++n) {
             double scale = (double)sx[m] * (double)sw[n];
             double v = (double)acc[m * N + n] * scale;
+            out[m * N + n] = oracle_bf16_rne_from_f64(v);
+        }
+    }
+}
+
+/*
+ * out[m,n] = bf16_rne(alpha * t + beta * bias[n]), t = acc[m,n] * (sx[m] * sw[n]),
+ * every operation a float64 operation in this order (no contraction); bias may
+ * be NULL, which means no bias term (beta is then ignored).
+ */
+void oracle_epilogue_addmm_bf16(const int32_t *acc, const float *sx, const float *sw,
+                                const float *bias, double alpha, double beta, int64_t M,
+                                int64_t N, uint16_t *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double scale = (double)sx[m] * (double)sw[n];
+            double t = (double)acc[m * N + n] * scale;
+            double v = alpha * t;
+            if (bias) v = v + beta * (double)bias[n];
             out[m * N + n] = oracle_bf16_rne_from_f64(v);
         }
     }

@@ -214,6 +214,55 @@ def test_epilogue_matches_exact_rationals(oracle):
             assert _bits_to_float(out[m, n]) == float(exact_bf16(exact)), (m, n)
 
 
+# --- addmm epilogue (bias, alpha, beta) ---------------------------------------
+
+def test_addmm_reduces_to_the_plain_epilogue(oracle):
+    """alpha = 1 with no bias term (or beta = 0) is the pinned plain epilogue, bit for bit."""
+    rng = np.random.default_rng(21)
+    acc = rng.integers(-2 ** 31, 2 ** 31, (17, 33), dtype=np.int64).astype(np.int32)
+    acc[0, :3] = [0, 1, -1]
+    sx = np.abs(rng.standard_normal(17)).astype(np.float32) * 1e-3
+    sw = np.abs(rng.standard_normal(33)).astype(np.float32) * 1e-3
+    bias = rng.standard_normal(33).astype(np.float32)
+    plain = oracle.epilogue_bf16(acc, sx, sw)
+    assert np.array_equal(oracle.epilogue_addmm_bf16(acc, sx, sw, None, 1.0, 0.0), plain)
+    assert np.array_equal(oracle.epilogue_addmm_bf16(acc, sx, sw, bias, 1.0, 0.0), plain)
+
+
+def test_addmm_hand_worked(oracle):
+    """acc = 100, sx = 0.5, sw = 0.25: acc*sx*sw = 12.5, worked by hand."""
+    acc = np.array([[100]], np.int32)
+    sx, sw = np.array([0.5], np.float32), np.array([0.25], np.float32)
+    cases = [  # bias, alpha, beta, value, bf16 bits
+        (-12.5, 2.0, 1.0, 12.5, 0x4148),   # 2 * 12.5 - 12.5
+        (-12.5, -1.0, 1.0, -25.0, 0xC1C8),  # -12.5 - 12.5
+        (3.0, 2.0, 0.5, 26.5, 0x41D4),      # 25 + 1.5
+        (-25.0, 2.0, 1.0, 0.0, 0x0000),     # exact cancellation: +0
+    ]
+    for b, alpha, beta, value, bits in cases:
+        out = oracle.epilogue_addmm_bf16(acc, sx, sw, np.array([b], np.float32), alpha, beta)
+        assert int(out[0, 0]) == bits, (b, alpha, beta, hex(int(out[0, 0])))
+        assert _bits_to_float(out[0, 0]) == value
+
+
+def test_addmm_matches_exact_rationals(oracle):
+    """alpha*acc*sx[m]*sw[n] + beta*bias[n], evaluated exactly, rounded once to bf16. M != N and
+    a bias that varies by channel catch a bias indexed by row or a dropped term."""
+    rng = np.random.default_rng(23)
+    M, N = 19, 41
+    acc = rng.integers(-2 ** 31, 2 ** 31, (M, N), dtype=np.int64).astype(np.int32)
+    sx = (np.abs(rng.standard_normal(M)) * 2.0 ** rng.integers(-30, -5, M)).astype(np.float32)
+    sw = (np.abs(rng.standard_normal(N)) * 2.0 ** rng.integers(-20, -5, N)).astype(np.float32)
+    bias = (rng.standard_normal(N) * 2.0 ** rng.integers(-4, 12, N)).astype(np.float32)
+    for alpha, beta in [(1.0, 1.0), (0.75, -2.5), (-3.0, 0.125)]:
+        out = oracle.epilogue_addmm_bf16(acc, sx, sw, bias, alpha, beta)
+        for m in range(M):
+            for n in range(N):
+                exact = (Fraction(alpha) * int(acc[m, n]) * Fraction(float(sx[m])) *
+                         Fraction(float(sw[n])) + Fraction(beta) * Fraction(float(bias[n])))
+                assert _bits_to_float(out[m, n]) == float(exact_bf16(exact)), (alpha, beta, m, n)
+
+
 def test_dequantized_product_error_bound(oracle):
     """|out - X W^T| is bounded by the quantization errors of X and W plus bf16 rounding."""
     inp = make_linear(24, 40, 96, seed=5)
