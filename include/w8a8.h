@@ -61,7 +61,8 @@ typedef enum {
     W8A8_ERR_K_OVERFLOW = -4, /* K > W8A8_MAX_K: int32 accumulation could overflow */
     W8A8_ERR_BLOCKSIZE = -5,  /* BSR block size other than 64 */
     W8A8_ERR_DTYPE = -6,      /* unknown output dtype selector */
-    W8A8_ERR_HIP = -7         /* the HIP runtime reported an error at launch */
+    W8A8_ERR_HIP = -7,        /* the HIP runtime reported an error at launch */
+    W8A8_ERR_VALUE = -8       /* a scalar argument (alpha, beta) is not finite */
 } w8a8_status;
 
 typedef enum {
@@ -109,6 +110,21 @@ w8a8_status w8a8_quantize_rows_f32(const float *x, int64_t M, int64_t K, int8_t 
 w8a8_status w8a8_gemm(const int8_t *xq, const float *x_scale, int64_t M, const int8_t *wq,
                       const float *w_scale, int64_t N, int64_t K, void *out,
                       w8a8_out_dtype out_dtype, void *stream);
+
+/*
+ * Dense W8A8 GEMM with an addmm epilogue (bf16 output):
+ *   out[m,n] = bf16_rne(alpha * (acc * x_scale[m] * w_scale[n]) + beta * bias[n])
+ * -- the beta / alpha of bsr_dense_addmm (pytorch/ao PR #821, the warning's
+ * "beta=0 alpha=1"), with bias a per-output-channel fp32 vector [N] as in a
+ * linear layer. bias may be NULL when beta == 0 (no bias term). The epilogue
+ * runs in fp32 in the kernel (within 1 bf16 ulp plus a few fp32 ulps of the
+ * two terms of the float64 definition). Other arguments as w8a8_gemm.
+ * Errors: NULL (also bias NULL with beta != 0), SHAPE, K_OVERFLOW, ALIGN
+ *         (bias included), VALUE (alpha or beta not finite), HIP.
+ */
+w8a8_status w8a8_gemm_addmm(const int8_t *xq, const float *x_scale, int64_t M, const int8_t *wq,
+                            const float *w_scale, int64_t N, int64_t K, const float *bias,
+                            float alpha, float beta, void *out, void *stream);
 
 /*
  * Block-sparse (BSR) W8A8 GEMM with the fused dequant epilogue: only stored

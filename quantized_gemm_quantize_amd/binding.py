@@ -23,6 +23,7 @@ W8A8_ERR_K_OVERFLOW = -4
 W8A8_ERR_BLOCKSIZE = -5
 W8A8_ERR_DTYPE = -6
 W8A8_ERR_HIP = -7
+W8A8_ERR_VALUE = -8
 W8A8_OUT_BF16 = 0
 W8A8_OUT_I32 = 1
 W8A8_MAX_K = 133136
@@ -53,7 +54,10 @@ def load():
     lib.w8a8_quantize_rows_f32.argtypes = [p, i64, i64, p, p, p]
     lib.w8a8_gemm.argtypes = [p, p, i64, p, p, i64, i64, p, i32, p]
     lib.w8a8_bsr_gemm.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, p, i32, p]
-    for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_bsr_gemm"):
+    f32 = ctypes.c_float
+    lib.w8a8_gemm_addmm.argtypes = [p, p, i64, p, p, i64, i64, p, f32, f32, p, p]
+    for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_gemm_addmm",
+               "w8a8_bsr_gemm"):
         getattr(lib, fn).restype = i32
     lib.w8a8_status_string.argtypes = [i32]
     lib.w8a8_status_string.restype = ctypes.c_char_p
@@ -144,6 +148,29 @@ def w8a8_gemm(xq, x_scale, wq, w_scale, out=None, out_dtype="bf16", stream=None)
     out = _out(out, M, N, od, xq.device)
     _call("w8a8_gemm", xq.data_ptr(), x_scale.data_ptr(), M, wq.data_ptr(), w_scale.data_ptr(),
           N, K, out.data_ptr(), od, _stream_handle(stream))
+    return out
+
+
+def w8a8_gemm_addmm(xq, x_scale, wq, w_scale, bias=None, alpha=1.0, beta=1.0, out=None,
+                    stream=None):
+    """out [M,N] = bf16(alpha * (sum_k xq[m,k] wq[n,k] * x_scale[m] * w_scale[n]) + beta * bias[n]);
+    bias None (allowed with beta == 0) means no bias term."""
+    _check_tensor(xq, "xq", torch.int8, 2)
+    _check_tensor(x_scale, "x_scale", torch.float32, 1)
+    _check_tensor(wq, "wq", torch.int8, 2)
+    _check_tensor(w_scale, "w_scale", torch.float32, 1)
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K2 != K or tuple(x_scale.shape) != (M,) or tuple(w_scale.shape) != (N,):
+        raise ValueError("operand shapes")
+    if bias is not None:
+        _check_tensor(bias, "bias", torch.float32, 1)
+        if tuple(bias.shape) != (N,):
+            raise ValueError("bias shape")
+    out = _out(out, M, N, _out_dtype("bf16"), xq.device)
+    _call("w8a8_gemm_addmm", xq.data_ptr(), x_scale.data_ptr(), M, wq.data_ptr(),
+          w_scale.data_ptr(), N, K, None if bias is None else bias.data_ptr(), float(alpha),
+          float(beta), out.data_ptr(), _stream_handle(stream))
     return out
 
 

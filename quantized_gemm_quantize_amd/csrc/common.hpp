@@ -48,6 +48,22 @@ __device__ __forceinline__ int xcd_contiguous(int pid, int tiles) {
     return base + idx;
 }
 
+// addmm epilogue of the GEMMs (bf16 output): out[m, n] = bf16(alpha * (acc *
+// sa[m] * sb[n]) + beta * bias[n]); no bias term when bias is null.
+struct Addmm {
+    const float *bias;
+    float alpha, beta;
+};
+
+template <bool ADDMM>
+__device__ __forceinline__ float addmm(float v, const Addmm &am, float b) {
+    if constexpr (ADDMM) {
+        v = am.alpha * v;
+        if (am.bias) v = v + am.beta * b;
+    }
+    return v;
+}
+
 // Workgroup barrier without a memory fence, for kernels whose loads go
 // straight to LDS: this wavefront's vector-memory operations up to the last N
 // have completed and its LDS operations are done, then all wavefronts meet.

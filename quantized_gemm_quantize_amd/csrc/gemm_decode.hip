@@ -21,11 +21,11 @@ namespace {
 
 constexpr int kUnroll = 8;   // K steps whose loads are issued together
 
-template <int MT, int KSPLIT, bool OUT_I32>
+template <int MT, int KSPLIT, bool OUT_I32, bool ADDMM>
 __global__ __launch_bounds__(KSPLIT *kWave) void gemm_decode_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ sa, const int8_t *__restrict__ B,
     const float *__restrict__ sb, void *__restrict__ out, int M, int N, int K,
-    int steps_per_wave) {
+    int steps_per_wave, Addmm am) {
     __shared__ int red[KSPLIT][MT][4][kWave];
 
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -80,7 +80,8 @@ __global__ __launch_bounds__(KSPLIT *kWave) void gemm_decode_kernel(
         if constexpr (OUT_I32) {
             static_cast<int32_t *>(out)[(int64_t)m * N + n] = sum;
         } else {
-            const float v = (float)sum * sa[m] * sb[n];
+            const float v =
+                addmm<ADDMM>((float)sum * sa[m] * sb[n], am, ADDMM && am.bias ? am.bias[n] : 0.0f);
             static_cast<__bf16 *>(out)[(int64_t)m * N + n] = (__bf16)v;
         }
     }
@@ -88,17 +89,21 @@ __global__ __launch_bounds__(KSPLIT *kWave) void gemm_decode_kernel(
 
 template <int MT>
 hipError_t launch_mt(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
-                     int N, int K, void *out, bool out_i32, hipStream_t stream) {
+                     int N, int K, void *out, bool out_i32, hipStream_t stream, const Addmm *am) {
     constexpr int KSPLIT = 8;
     const int total_steps = (K + 63) / 64;
     const int steps_per_wave = (total_steps + KSPLIT - 1) / KSPLIT;
     const dim3 grid((unsigned)(N / 16)), block(KSPLIT * kWave);
+    const Addmm a = am ? *am : Addmm{nullptr, 1.0f, 0.0f};
     if (out_i32)
-        gemm_decode_kernel<MT, KSPLIT, true>
-            <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, steps_per_wave);
+        gemm_decode_kernel<MT, KSPLIT, true, false>
+            <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, steps_per_wave, a);
+    else if (am)
+        gemm_decode_kernel<MT, KSPLIT, false, true>
+            <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, steps_per_wave, a);
     else
-        gemm_decode_kernel<MT, KSPLIT, false>
-            <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, steps_per_wave);
+        gemm_decode_kernel<MT, KSPLIT, false, false>
+            <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, steps_per_wave, a);
     return hipGetLastError();
 }
 
@@ -106,12 +111,12 @@ hipError_t launch_mt(const int8_t *xq, const float *xs, int M, const int8_t *wq,
 
 hipError_t launch_gemm_decode(const int8_t *xq, const float *xs, int M, const int8_t *wq,
                               const float *ws, int N, int K, void *out, bool out_i32,
-                              hipStream_t stream) {
+                              hipStream_t stream, const Addmm *am) {
     switch ((M + 15) / 16) {
-        case 1: return launch_mt<1>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
-        case 2: return launch_mt<2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
-        case 3: return launch_mt<3>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
-        default: return launch_mt<4>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
+        case 1: return launch_mt<1>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
+        case 2: return launch_mt<2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
+        case 3: return launch_mt<3>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
+        default: return launch_mt<4>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
     }
 }
 

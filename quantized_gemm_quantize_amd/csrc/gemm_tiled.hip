@@ -194,11 +194,13 @@ __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool KTAIL, bool OUT_I32>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool KTAIL, bool OUT_I32,
+          bool ADDMM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ sa, const int8_t *__restrict__ B,
     const float *__restrict__ sb, void *__restrict__ out, int M, int N, int K, int tiles_m,
-    int tiles_n) {
+    int tiles_n, Addmm am) {
+    static_assert(!(ADDMM && OUT_I32), "the addmm epilogue writes bf16");
     static_assert(WAVES_M * WAVES_N == kWaves, "4 wavefronts");
     static_assert(STAGES == 2 || STAGES == 3, "double or triple buffering");
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -320,32 +322,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
         constexpr int CH = WN / 8;  // 16-byte chunks per staged row
         static_assert(CH >= 8, "the row-chunk permutation needs 8 chunks per row");
         uint2 *st8 = reinterpret_cast<uint2 *>(lds) + wave * (WM * WN / 4);
-        float swv[TN][4][4];
+        // per 4 channels: their scales (and bias) once, then the TM rows
+        float sxv[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sxv[i] = sa[min(mw0 + i * 32 + frag_row, M - 1)];
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = min(nw0 + j * 32 + 8 * g + 4 * half, N - 4);
-                const float4 v = *reinterpret_cast<const float4 *>(sb + n);
-                swv[j][g][0] = v.x; swv[j][g][1] = v.y; swv[j][g][2] = v.z; swv[j][g][3] = v.w;
-            }
+                const float4 w = *reinterpret_cast<const float4 *>(sb + n);
+                float4 bv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (ADDMM && am.bias) bv = *reinterpret_cast<const float4 *>(am.bias + n);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int ml = i * 32 + frag_row;
-            const float sxv = sa[min(mw0 + ml, M - 1)];
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
+                for (int i = 0; i < TM; ++i) {
+                    const int ml = i * 32 + frag_row;
                     const v16i &a = acc[i][j];
-                    const uint32_t lo = pack_bf16x2((float)a[4 * g] * sxv * swv[j][g][0],
-                                                    (float)a[4 * g + 1] * sxv * swv[j][g][1]);
-                    const uint32_t hi = pack_bf16x2((float)a[4 * g + 2] * sxv * swv[j][g][2],
-                                                    (float)a[4 * g + 3] * sxv * swv[j][g][3]);
+                    const uint32_t lo =
+                        pack_bf16x2(addmm<ADDMM>((float)a[4 * g] * sxv[i] * w.x, am, bv.x),
+                                    addmm<ADDMM>((float)a[4 * g + 1] * sxv[i] * w.y, am, bv.y));
+                    const uint32_t hi =
+                        pack_bf16x2(addmm<ADDMM>((float)a[4 * g + 2] * sxv[i] * w.z, am, bv.z),
+                                    addmm<ADDMM>((float)a[4 * g + 3] * sxv[i] * w.w, am, bv.w));
                     const int chunk = (j * 4 + g) ^ (ml & 7);
                     st8[(ml * CH + chunk) * 2 + half] = make_uint2(lo, hi);
                 }
-        }
+            }
         __syncthreads();
         const uint4 *st16 = reinterpret_cast<const uint4 *>(st8);
 #pragma unroll
@@ -362,25 +364,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool KTAIL>
 void launch_tail(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
-                 int N, int K, void *out, bool out_i32, hipStream_t stream) {
+                 int N, int K, void *out, bool out_i32, hipStream_t stream, const Addmm *am) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
+    const Addmm a = am ? *am : Addmm{nullptr, 1.0f, 0.0f};
     if (out_i32)
-        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, KTAIL, true>
-            <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, tiles_m, tiles_n);
+        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, KTAIL, true, false>
+            <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, tiles_m, tiles_n, a);
+    else if (am)
+        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, KTAIL, false, true>
+            <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, tiles_m, tiles_n, a);
     else
-        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, KTAIL, false>
-            <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, tiles_m, tiles_n);
+        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, KTAIL, false, false>
+            <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, tiles_m, tiles_n, a);
 }
 
 // K % 128 != 0 takes the variant that zeroes the chunks past K.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 hipError_t launch_cfg(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
-                      int N, int K, void *out, bool out_i32, hipStream_t stream) {
+                      int N, int K, void *out, bool out_i32, hipStream_t stream, const Addmm *am) {
     if (K % kBK == 0)
-        launch_tail<BM, BN, WAVES_M, WAVES_N, STAGES, false>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
+        launch_tail<BM, BN, WAVES_M, WAVES_N, STAGES, false>(xq, xs, M, wq, ws, N, K, out, out_i32,
+                                                             stream, am);
     else
-        launch_tail<BM, BN, WAVES_M, WAVES_N, STAGES, true>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
+        launch_tail<BM, BN, WAVES_M, WAVES_N, STAGES, true>(xq, xs, M, wq, ws, N, K, out, out_i32,
+                                                            stream, am);
     return hipGetLastError();
 }
 
@@ -388,18 +396,18 @@ hipError_t launch_cfg(const int8_t *xq, const float *xs, int M, const int8_t *wq
 
 hipError_t launch_gemm_decode(const int8_t *xq, const float *xs, int M, const int8_t *wq,
                               const float *ws, int N, int K, void *out, bool out_i32,
-                              hipStream_t stream);
+                              hipStream_t stream, const Addmm *am);
 
 hipError_t launch_gemm(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
-                       int N, int K, void *out, bool out_i32, hipStream_t stream) {
-    if (M <= 64) return launch_gemm_decode(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
+                       int N, int K, void *out, bool out_i32, hipStream_t stream, const Addmm *am) {
+    if (M <= 64) return launch_gemm_decode(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
     // Enough 256x256 tiles to fill 256 CUs several times over: the big tile
     // halves LDS traffic per MFMA. Otherwise 256x128 (or 128x128) tiles.
     const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
     const long t128 = (long)((M + 255) / 256) * ((N + 127) / 128);
-    if (t256 >= 4 * 256) return launch_cfg<256, 256, 2, 2, 2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
-    if (t128 >= 256) return launch_cfg<256, 128, 2, 2, 3>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
-    return launch_cfg<128, 128, 2, 2, 2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream);
+    if (t256 >= 4 * 256) return launch_cfg<256, 256, 2, 2, 2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
+    if (t128 >= 256) return launch_cfg<256, 128, 2, 2, 3>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
+    return launch_cfg<128, 128, 2, 2, 2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
 }
 
 }  // namespace w8a8

@@ -12,10 +12,14 @@ hipError_t launch_quantize_rows_bf16(const uint16_t *x, int64_t M, int K, int8_t
 hipError_t launch_quantize_rows_f32(const float *x, int64_t M, int K, int8_t *xq, float *xs,
                                     hipStream_t stream);
 
+struct Addmm;
+
 // Dense GEMM: picks the weight-streaming kernel for M <= 64, the LDS-tiled
-// MFMA kernel otherwise.
+// MFMA kernel otherwise. With am non-null (bf16 output only) the epilogue is
+// alpha * (acc * sa * sb) + beta * bias.
 hipError_t launch_gemm(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
-                       int N, int K, void *out, bool out_i32, hipStream_t stream);
+                       int N, int K, void *out, bool out_i32, hipStream_t stream,
+                       const Addmm *am = nullptr);
 
 // Compute units of the current device (queried once per device).
 int device_cu_count();

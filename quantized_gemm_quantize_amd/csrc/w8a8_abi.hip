@@ -10,7 +10,9 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cmath>
 
+#include "common.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -99,6 +101,24 @@ w8a8_status w8a8_gemm(const int8_t *xq, const float *x_scale, int64_t M, const i
                                         static_cast<hipStream_t>(stream)));
 }
 
+w8a8_status w8a8_gemm_addmm(const int8_t *xq, const float *x_scale, int64_t M, const int8_t *wq,
+                            const float *w_scale, int64_t N, int64_t K, const float *bias,
+                            float alpha, float beta, void *out, void *stream) {
+    if (M < 0 || N <= 0 || N % 16 != 0 || too_big(M, N)) return W8A8_ERR_SHAPE;
+    if (w8a8_status s = check_k(K)) return s;
+    if (!std::isfinite(alpha) || !std::isfinite(beta)) return W8A8_ERR_VALUE;
+    if ((M + 127) / 128 > INT_MAX / ((N + 127) / 128)) return W8A8_ERR_SHAPE;  // grid.x
+    if (M == 0) return W8A8_OK;
+    if (!xq || !x_scale || !wq || !w_scale || !out) return W8A8_ERR_NULL;
+    if (!bias && beta != 0.0f) return W8A8_ERR_NULL;
+    if (misaligned(xq) || misaligned(x_scale) || misaligned(wq) || misaligned(w_scale) ||
+        misaligned(out) || (bias && misaligned(bias)))
+        return W8A8_ERR_ALIGN;
+    const w8a8::Addmm am{bias, alpha, beta};
+    return hip_status(w8a8::launch_gemm(xq, x_scale, (int)M, wq, w_scale, (int)N, (int)K, out,
+                                        false, static_cast<hipStream_t>(stream), &am));
+}
+
 w8a8_status w8a8_bsr_gemm(const int8_t *xq, const float *x_scale, int64_t M, int64_t K,
                           const int32_t *crow, const int32_t *col, const int8_t *values,
                           int64_t nnzb, int64_t bs, const float *w_scale, int64_t N, void *out,
@@ -132,6 +152,7 @@ const char *w8a8_status_string(int status) {
         case W8A8_ERR_BLOCKSIZE: return "BSR block size must be 64";
         case W8A8_ERR_DTYPE: return "unknown output dtype";
         case W8A8_ERR_HIP: return "HIP launch error (see w8a8_last_hip_error)";
+        case W8A8_ERR_VALUE: return "alpha or beta is not finite";
         default: return "unknown status";
     }
 }

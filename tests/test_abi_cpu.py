@@ -13,7 +13,7 @@ from quantized_gemm_quantize_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w8a8.h")
 
-OK, NULL, SHAPE, ALIGN, KOVF, BLK, DTYPE = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, SHAPE, ALIGN, KOVF, BLK, DTYPE, VALUE = 0, -1, -2, -3, -4, -5, -6, -8
 P = 0x10000  # an aligned, never-dereferenced stand-in for a device pointer
 
 
@@ -31,8 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_bsr_gemm",
-               "w8a8_status_string", "w8a8_last_hip_error"):
+    for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_gemm_addmm",
+               "w8a8_bsr_gemm", "w8a8_status_string", "w8a8_last_hip_error"):
         assert fn in names
 
 
@@ -47,13 +47,13 @@ def test_header_constants_match_binding():
     assert 127 * 127 * binding.W8A8_MAX_K < 2 ** 31
     assert 127 * 127 * (binding.W8A8_MAX_K + 16) >= 2 ** 31
     for name in ("W8A8_ERR_NULL", "W8A8_ERR_SHAPE", "W8A8_ERR_ALIGN", "W8A8_ERR_K_OVERFLOW",
-                 "W8A8_ERR_BLOCKSIZE", "W8A8_ERR_DTYPE", "W8A8_ERR_HIP"):
+                 "W8A8_ERR_BLOCKSIZE", "W8A8_ERR_DTYPE", "W8A8_ERR_HIP", "W8A8_ERR_VALUE"):
         m = re.search(rf"{name}\s*=\s*(-?\d+)", text)
         assert int(m.group(1)) == getattr(binding, name)
 
 
 def test_status_strings(lib):
-    for st in (OK, NULL, SHAPE, ALIGN, KOVF, BLK, DTYPE, -7, 99):
+    for st in (OK, NULL, SHAPE, ALIGN, KOVF, BLK, DTYPE, -7, VALUE, 99):
         assert lib.w8a8_status_string(st)
     assert lib.w8a8_last_hip_error() == 0
 
@@ -90,6 +90,24 @@ def test_gemm_validation(lib):
         assert g(*args(**{k: 0})) == NULL, k
         assert g(*args(**{k: P + 4})) == ALIGN, k
     assert g(*args(M=0, xq=0, xs=0, out=0)) == OK       # empty: no launch
+
+
+def test_gemm_addmm_validation(lib):
+    g = lib.w8a8_gemm_addmm
+    args = lambda **kw: [kw.get("xq", P), kw.get("xs", P), kw.get("M", 32), kw.get("wq", P),
+                         kw.get("ws", P), kw.get("N", 64), kw.get("K", 64), kw.get("bias", P),
+                         kw.get("alpha", 1.0), kw.get("beta", 1.0), kw.get("out", P), None]
+    assert g(*args(M=-1)) == SHAPE
+    assert g(*args(N=40)) == SHAPE
+    assert g(*args(K=72)) == SHAPE
+    assert g(*args(K=133152)) == KOVF
+    assert g(*args(alpha=float("inf"))) == VALUE
+    assert g(*args(beta=float("nan"))) == VALUE
+    for k in ("xq", "xs", "wq", "ws", "out", "bias"):
+        assert g(*args(**{k: 0})) == NULL, k
+        assert g(*args(**{k: P + 4})) == ALIGN, k
+    assert g(*args(bias=0, beta=0.0, M=0)) == OK        # no bias term, empty: no launch
+    assert g(*args(M=0, xq=0, xs=0, out=0)) == OK
 
 
 def test_bsr_validation(lib):

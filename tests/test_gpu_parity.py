@@ -232,6 +232,55 @@ def test_gemm_deterministic(b, oracle):
         assert torch.equal(first.view(torch.int16), again.view(torch.int16))
 
 
+# --- addmm epilogue ---------------------------------------------------------
+
+def _bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |x| (8 significant bits, binary32 exponents)."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (16, 256, 512), (64, 128, 256), (300, 512, 320),
+                                   (129, 1024, 4096)])
+@pytest.mark.parametrize("alpha,beta,with_bias", [(1.0, 1.0, True), (0.5, -2.0, True),
+                                                  (-1.25, 0.0, True), (2.0, 0.0, False)])
+def test_gemm_addmm(b, oracle, M, N, K, alpha, beta, with_bias):
+    """GPU addmm epilogue against the oracle's float64 definition: within one bf16 ulp plus
+    2^-20 of |alpha * acc * sx * sw| + |beta * bias| (the fp32 rounding of the two terms)."""
+    log(f"gemm addmm M={M} N={N} K={K} alpha={alpha} beta={beta} bias={with_bias}")
+    inp = make_linear(M, N, K, seed=M + N + K + 7)
+    xq, sx, xq_ref, sx_ref = _check_quantize(b, oracle, inp.x_bits, "addmm X")
+    wq, sw, wq_ref, sw_ref = gpu_weights(b, oracle, inp.w)
+    rng = np.random.default_rng(M * 7 + N)
+    bias = (rng.standard_normal(N) * 0.5).astype(np.float32) if with_bias else None
+    bias_dev = torch.from_numpy(bias).to(DEV) if with_bias else None
+    got = bf16_bits(b.w8a8_gemm_addmm(xq, sx, wq, sw, bias=bias_dev, alpha=alpha, beta=beta))
+    acc = oracle.gemm_i32(xq_ref, wq_ref)
+    ref = oracle.epilogue_addmm_bf16(acc, sx_ref, sw_ref, bias, alpha, beta)
+    g = bf16_bits_to_f32(got).astype(np.float64)
+    o = bf16_bits_to_f32(ref).astype(np.float64)
+    t = acc.astype(np.float64) * sx_ref.astype(np.float64)[:, None] * sw_ref.astype(np.float64)[None, :]
+    mag = np.abs(alpha * t)
+    if with_bias:
+        mag = mag + np.abs(beta * bias.astype(np.float64))[None, :]
+    bound = _bf16_ulp(np.maximum(np.abs(g), np.abs(o))) + mag * 2.0 ** -20
+    worst = np.max(np.abs(g - o) - bound)
+    assert (np.abs(g - o) <= bound).all(), worst
+    if alpha == 1.0 and not with_bias:
+        assert np.array_equal(got, bf16_bits(b.w8a8_gemm(xq, sx, wq, sw)))
+
+
+def test_gemm_addmm_identity_is_the_plain_gemm(b, oracle):
+    """alpha = 1 with no bias runs the addmm kernels and gives the plain epilogue bit for bit."""
+    for M in (16, 300):
+        inp = make_linear(M, 256, 512, seed=3)
+        xq, sx = b.w8a8_quantize_rows(to_dev_bf16(inp.x_bits))
+        wq, sw = b.w8a8_quantize_rows_f32(torch.from_numpy(inp.w).to(DEV))
+        plain = b.w8a8_gemm(xq, sx, wq, sw)
+        am = b.w8a8_gemm_addmm(xq, sx, wq, sw, bias=None, alpha=1.0, beta=0.0)
+        assert torch.equal(plain.view(torch.int16), am.view(torch.int16)), M
+
+
 # --- block-sparse GEMM ------------------------------------------------------
 
 def _bsr_case(b, oracle, M, N, K, zero_frac, seed, rows=None):
