@@ -15,7 +15,9 @@ The line also carries:
   cpu_baseline the CPU oracle timed on this host on a bounded sample;
   decode_m16   the M=16 weight-streaming path (K=N=4096): GB/s of the GEMM
                kernel against HBM peak, with rotated weight copies so the
-               256 MB Infinity Cache cannot serve them.
+               256 MB Infinity Cache cannot serve them; the two-launch layer
+               (quantize + GEMM) and the single-launch w8a8_fused_linear, both
+               priced at the layer's bytes (X bf16 + Wq + sw + out).
 
 Inputs are resident in HBM before the timed region; input sets are rotated
 (copies at distinct addresses, more than twice the Infinity Cache in total).
@@ -188,10 +190,20 @@ def bench_decode(torch, np, b, dev, steps, warmup, eager=False):
         b.w8a8_quantize_rows(d["x"], xq2, sx2)
         b.w8a8_gemm(xq2, sx2, wqs[i % R], d["sw"], out=out)
 
+    fused = lambda i: b.w8a8_fused_linear(d["x"], wqs[i % R], d["sw"], beta=0.0, out=out)
+
     for i in range(warmup):
         step(i)
+        fused(i)
+    # the single launch gives the two-launch step's output bit for bit
+    step(0)
+    two = out.clone()
+    fused(0)
+    if not torch.equal(two.view(torch.int16), out.view(torch.int16)):
+        raise SystemExit("fused linear differs from quantize_rows + gemm")
     ms_gemm = time_median(gemm, steps, torch, R, eager)
     ms_step = time_median(step, steps, torch, R, eager)
+    ms_fused = time_median(fused, steps, torch, R, eager)
     gemm_bytes = M * K + 4 * M + N * K + 4 * N + 2 * M * N
     layer_bytes = 2 * M * K + N * K + 4 * N + 2 * M * N
     gbs = gemm_bytes / (ms_gemm * 1e-3) / 1e9
@@ -199,7 +211,9 @@ def bench_decode(torch, np, b, dev, steps, warmup, eager=False):
             "gemm_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "gemm_bytes": gemm_bytes, "step_us": round(ms_step * 1e3, 3),
             "step_GBps": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
-            "weight_copies_rotated": R}
+            "fused_linear_us": round(ms_fused * 1e3, 3),
+            "fused_linear_GBps": round(layer_bytes / (ms_fused * 1e-3) / 1e9, 1),
+            "layer_bytes": layer_bytes, "weight_copies_rotated": R}
 
 
 def main():

@@ -126,6 +126,33 @@ w8a8_status w8a8_gemm_addmm(const int8_t *xq, const float *x_scale, int64_t M, c
                             const float *w_scale, int64_t N, int64_t K, const float *bias,
                             float alpha, float beta, void *out, void *stream);
 
+/* Largest M taken by w8a8_fused_linear. */
+#define W8A8_FUSED_MAX_M 64
+
+/*
+ * Single-launch dynamically quantized linear layer for small batches
+ * (decode): quantize_rows of x_bf16 fused into the GEMM, with the addmm
+ * epilogue of w8a8_gemm_addmm:
+ *   out[m,n] = bf16_rne(alpha * (acc * s[m] * w_scale[n]) + beta * bias[n]),
+ *   acc = sum_k q[m,k] * wq[n,k], with q and s exactly as w8a8_quantize_rows
+ *   computes them (the codes and scales are not written out).
+ * One launch instead of quantize + GEMM, with no intermediate buffers: the
+ * quantization is the scaling work that pytorch/ao PR #821 asks to move into
+ * the kernel. Every workgroup of the kernel quantizes all of x, so on MI355X
+ * it is slower than w8a8_quantize_rows followed by w8a8_gemm (at M = 16,
+ * K = N = 4096: about 15 us against 11 us); it serves callers that cannot
+ * hold the int8 codes and scales between two calls.
+ *   x_bf16  [M,K] bf16 row-major, 0 <= M <= W8A8_FUSED_MAX_M
+ *   wq, w_scale, bias, alpha, beta, out as for w8a8_gemm_addmm (bias NULL,
+ *   alpha 1, beta 0: the plain fused dequant epilogue).
+ * Larger M: w8a8_quantize_rows, then w8a8_gemm or w8a8_gemm_addmm.
+ * Errors: NULL (also bias NULL with beta != 0), SHAPE (M > W8A8_FUSED_MAX_M
+ *         and as w8a8_gemm), K_OVERFLOW, ALIGN, VALUE, HIP.
+ */
+w8a8_status w8a8_fused_linear(const void *x_bf16, int64_t M, int64_t K, const int8_t *wq,
+                              const float *w_scale, int64_t N, const float *bias, float alpha,
+                              float beta, void *out, void *stream);
+
 /*
  * Block-sparse (BSR) W8A8 GEMM with the fused dequant epilogue: only stored
  * weight blocks are read and multiplied; output channels of block rows with

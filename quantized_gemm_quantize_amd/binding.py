@@ -27,6 +27,7 @@ W8A8_ERR_VALUE = -8
 W8A8_OUT_BF16 = 0
 W8A8_OUT_I32 = 1
 W8A8_MAX_K = 133136
+W8A8_FUSED_MAX_M = 64
 
 _lib = None
 
@@ -56,8 +57,9 @@ def load():
     lib.w8a8_bsr_gemm.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, p, i32, p]
     f32 = ctypes.c_float
     lib.w8a8_gemm_addmm.argtypes = [p, p, i64, p, p, i64, i64, p, f32, f32, p, p]
+    lib.w8a8_fused_linear.argtypes = [p, i64, i64, p, p, i64, p, f32, f32, p, p]
     for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_gemm_addmm",
-               "w8a8_bsr_gemm"):
+               "w8a8_fused_linear", "w8a8_bsr_gemm"):
         getattr(lib, fn).restype = i32
     lib.w8a8_status_string.argtypes = [i32]
     lib.w8a8_status_string.restype = ctypes.c_char_p
@@ -196,7 +198,32 @@ def w8a8_bsr_gemm(xq, x_scale, crow, col, values, w_scale, out=None, out_dtype="
     return out
 
 
+def w8a8_fused_linear(x, wq, w_scale, bias=None, alpha=1.0, beta=1.0, out=None, stream=None):
+    """Single-launch quantize + GEMM for x [M,K] bf16 with M <= 64:
+    out = bf16(alpha * (acc * s[m] * w_scale[n]) + beta * bias[n]), q and s as
+    w8a8_quantize_rows computes them; bias None (allowed with beta == 0) means
+    no bias term."""
+    _check_tensor(x, "x", torch.bfloat16, 2)
+    _check_tensor(wq, "wq", torch.int8, 2)
+    _check_tensor(w_scale, "w_scale", torch.float32, 1)
+    M, K = x.shape
+    N, K2 = wq.shape
+    if K2 != K or tuple(w_scale.shape) != (N,):
+        raise ValueError("operand shapes")
+    if bias is not None:
+        _check_tensor(bias, "bias", torch.float32, 1)
+        if tuple(bias.shape) != (N,):
+            raise ValueError("bias shape")
+    out = _out(out, M, N, _out_dtype("bf16"), x.device)
+    _call("w8a8_fused_linear", x.data_ptr(), M, K, wq.data_ptr(), w_scale.data_ptr(), N,
+          None if bias is None else bias.data_ptr(), float(alpha), float(beta), out.data_ptr(),
+          _stream_handle(stream))
+    return out
+
+
 def w8a8_linear(x, wq, w_scale, out=None, stream=None):
-    """Dynamically quantized linear layer: quantize_rows(x) then the fused GEMM."""
+    """Dynamically quantized linear layer: quantize_rows(x), then the fused-dequant GEMM.
+    (Two launches are faster than w8a8_fused_linear at every M it takes: each of its
+    N/16 workgroups quantizes all of x.)"""
     xq, xs = w8a8_quantize_rows(x, stream=stream)
     return w8a8_gemm(xq, xs, wq, w_scale, out=out, stream=stream)

@@ -13,8 +13,22 @@
 //  - the K-split partial int32 tiles are summed in LDS (never in HBM), then
 //    scaled, rounded to bf16 and stored: the same fused epilogue as the tiled
 //    kernel.
-#include "common.hpp"
+//
+// The single-launch linear (linear_decode_kernel) is the same kernel with the
+// activation quantization moved into its prologue (pytorch/ao PR #821 asks for
+// scaling inside the kernel), so no intermediate codes or scales leave the
+// chip. Each lane loads the bf16 activations of exactly the fragment
+// positions it multiplies, before its weight loads: vector loads return in
+// order, so the row absmax, its reduction across the workgroup (shuffles, then
+// LDS) and the quantization run while the weight bytes are still on their way
+// from HBM. Every workgroup quantizes all M rows itself (the rows are L2 hits
+// after the first), with the arithmetic of quant_math.hpp, so its codes and
+// scales are the ones w8a8_quantize_rows writes. That redundancy is the cost:
+// each CU runs about eight vector instructions for each of the M * K
+// activations, which at M = 16, K = N = 4096 takes longer than the separate
+// quantize launch it replaces.
 #include "launch.hpp"
+#include "quant_math.hpp"
 
 namespace w8a8 {
 namespace {
@@ -87,6 +101,162 @@ __global__ __launch_bounds__(KSPLIT *kWave) void gemm_decode_kernel(
     }
 }
 
+constexpr int kLinSplit = 8;  // wavefronts per workgroup (K split) of the fused linear
+
+template <int MT, int U, bool ADDMM>
+__global__ __launch_bounds__(kLinSplit *kWave) void linear_decode_kernel(
+    const uint16_t *__restrict__ X, const int8_t *__restrict__ B, const float *__restrict__ sb,
+    __bf16 *__restrict__ out, int M, int N, int K, int steps_per_wave, Addmm am) {
+    __shared__ int red[kLinSplit][MT][4][kWave];
+    __shared__ uint32_t red_amax[kLinSplit][MT * 16];
+    __shared__ float row_s[MT * 16];
+
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int n0 = blockIdx.x * 16;
+    const int r16 = lane & 15, kgrp = lane >> 4;
+    const int8_t *brow = B + (int64_t)(n0 + r16) * K;
+    const uint16_t *xrow[MT];
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) xrow[mb] = X + (int64_t)min(mb * 16 + r16, M - 1) * K;
+
+    const int total_steps = (K + 63) / 64;
+    const int s_begin = wave * steps_per_wave;
+    const int s_end = min(s_begin + steps_per_wave, total_steps);
+    const int nchunk = s_end > s_begin ? (s_end - s_begin + U - 1) / U : 0;  // uniform
+
+    // K step s: this lane's 16 elements start at s * 64 + 16 * kgrp; past K
+    // (or past the wavefront's steps) the activations count as zeros. Loads
+    // always read in bounds (offset clamped into the row) so they stay
+    // unconditional 16-byte loads, issued before anything waits on them. A
+    // clamped activation is an element of the same row, so it leaves the
+    // absmax unchanged; the activation codes of such steps are zeroed before
+    // the MFMA, which also cancels whatever weight bytes the clamped load
+    // returned.
+    auto k_ok = [&](int s) { return s < s_end && s * 64 + kgrp * 16 < K; };
+    auto k_off = [&](int s) { return min(s * 64 + kgrp * 16, K - 16); };
+    v4i xr[MT][U][2];
+    v4i b[U];
+    auto load_chunk = [&](int s) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int mb = 0; mb < MT; ++mb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    xr[mb][u][h] = *reinterpret_cast<const v4i *>(xrow[mb] + k_off(s + u) + 8 * h);
+        __builtin_amdgcn_sched_barrier(0);  // activations first, then weights
+#pragma unroll
+        for (int u = 0; u < U; ++u) b[u] = *reinterpret_cast<const v4i *>(brow + k_off(s + u));
+        __builtin_amdgcn_sched_barrier(0);  // all issued before anything waits on them
+    };
+
+    // row absmax over this lane's positions; a wavefront with more than one
+    // chunk of K steps reads its later chunks here once more, absmax only
+    uint32_t amax[MT];
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) amax[mb] = 0;
+    if (nchunk > 0) {
+        load_chunk(s_begin);
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                absmax8(__builtin_bit_cast(uint4, xr[mb][u][0]), amax[mb]);
+                absmax8(__builtin_bit_cast(uint4, xr[mb][u][1]), amax[mb]);
+            }
+        for (int c = 1; c < nchunk; ++c) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int st = s_begin + c * U + u;
+#pragma unroll
+                for (int mb = 0; mb < MT; ++mb)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        absmax8(*reinterpret_cast<const uint4 *>(xrow[mb] + k_off(st) + 8 * h),
+                                amax[mb]);
+            }
+        }
+    }
+    // lanes r16, r16 + 16, r16 + 32, r16 + 48 share a row; then the wavefronts
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) {
+        amax[mb] = max(amax[mb], (uint32_t)__shfl_xor((int)amax[mb], 16, kWave));
+        amax[mb] = max(amax[mb], (uint32_t)__shfl_xor((int)amax[mb], 32, kWave));
+        if (lane < 16) red_amax[wave][mb * 16 + lane] = amax[mb];
+    }
+    __syncthreads();
+    RowScale rs[MT];
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) {
+        uint32_t a = 0;
+#pragma unroll
+        for (int w = 0; w < kLinSplit; ++w) a = max(a, red_amax[w][mb * 16 + r16]);
+        rs[mb] = row_scale(__uint_as_float(a));
+        if (wave == 0 && lane < 16) row_s[mb * 16 + lane] = rs[mb].s;
+    }
+
+    v4i acc[MT];
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) acc[mb] = v4i{};
+    for (int c = 0; c < nchunk; ++c) {
+        if (c > 0) load_chunk(s_begin + c * U);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = k_ok(s_begin + c * U + u);
+#pragma unroll
+            for (int mb = 0; mb < MT; ++mb) {
+                float v[8];
+                widen8(__builtin_bit_cast(uint4, xr[mb][u][0]), v);
+                const uint2 q0 = quantize8(v, rs[mb]);
+                widen8(__builtin_bit_cast(uint4, xr[mb][u][1]), v);
+                const uint2 q1 = quantize8(v, rs[mb]);
+                const v4i a = {(int)q0.x, (int)q0.y, (int)q1.x, (int)q1.y};
+                acc[mb] = mfma_16x16x64(ok ? a : v4i{}, b[u], acc[mb]);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][mb][r][lane] = acc[mb][r];
+    __syncthreads();
+
+    for (int e = threadIdx.x; e < MT * 256; e += kLinSplit * kWave) {
+        const int mb = e >> 8, i = (e >> 4) & 15, j = e & 15;
+        const int m = mb * 16 + i;
+        if (m >= M) continue;
+        const int l = j + 16 * (i >> 2), r = i & 3;
+        int sum = 0;
+#pragma unroll
+        for (int w = 0; w < kLinSplit; ++w) sum += red[w][mb][r][l];
+        const int n = n0 + j;
+        const float v =
+            addmm<ADDMM>((float)sum * row_s[m] * sb[n], am, ADDMM && am.bias ? am.bias[n] : 0.0f);
+        out[(int64_t)m * N + n] = (__bf16)v;
+    }
+}
+
+template <int MT>
+hipError_t launch_linear_mt(const uint16_t *x, int M, const int8_t *wq, const float *ws, int N,
+                            int K, void *out, hipStream_t stream, const Addmm &am) {
+    // K steps per chunk: a lane holds MT * U * 32 activation bytes while the
+    // chunk's weights are in flight (64 registers), so M <= 16 covers K = 4096
+    // in one chunk; more row blocks take shorter chunks (no register spills)
+    constexpr int U = MT == 1 ? 8 : MT == 2 ? 4 : 2;
+    const int total_steps = (K + 63) / 64;
+    const int steps_per_wave = (total_steps + kLinSplit - 1) / kLinSplit;
+    const dim3 grid((unsigned)(N / 16)), block(kLinSplit * kWave);
+    __bf16 *o = static_cast<__bf16 *>(out);
+    if (am.bias || am.alpha != 1.0f)
+        linear_decode_kernel<MT, U, true>
+            <<<grid, block, 0, stream>>>(x, wq, ws, o, M, N, K, steps_per_wave, am);
+    else
+        linear_decode_kernel<MT, U, false>
+            <<<grid, block, 0, stream>>>(x, wq, ws, o, M, N, K, steps_per_wave, am);
+    return hipGetLastError();
+}
+
 template <int MT>
 hipError_t launch_mt(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
                      int N, int K, void *out, bool out_i32, hipStream_t stream, const Addmm *am) {
@@ -108,6 +278,16 @@ hipError_t launch_mt(const int8_t *xq, const float *xs, int M, const int8_t *wq,
 }
 
 }  // namespace
+
+hipError_t launch_linear_decode(const uint16_t *x, int M, const int8_t *wq, const float *ws, int N,
+                                int K, void *out, hipStream_t stream, const Addmm &am) {
+    switch ((M + 15) / 16) {
+        case 1: return launch_linear_mt<1>(x, M, wq, ws, N, K, out, stream, am);
+        case 2: return launch_linear_mt<2>(x, M, wq, ws, N, K, out, stream, am);
+        case 3: return launch_linear_mt<3>(x, M, wq, ws, N, K, out, stream, am);
+        default: return launch_linear_mt<4>(x, M, wq, ws, N, K, out, stream, am);
+    }
+}
 
 hipError_t launch_gemm_decode(const int8_t *xq, const float *xs, int M, const int8_t *wq,
                               const float *ws, int N, int K, void *out, bool out_i32,

@@ -21,6 +21,11 @@ hipError_t launch_gemm(const int8_t *xq, const float *xs, int M, const int8_t *w
                        int N, int K, void *out, bool out_i32, hipStream_t stream,
                        const Addmm *am = nullptr);
 
+// Single-launch linear for M <= 64: quantize_rows of bf16 X fused into the
+// weight-streaming GEMM, epilogue as launch_gemm's with am.
+hipError_t launch_linear_decode(const uint16_t *x, int M, const int8_t *wq, const float *ws, int N,
+                                int K, void *out, hipStream_t stream, const Addmm &am);
+
 // Compute units of the current device (queried once per device).
 int device_cu_count();
 

@@ -12,22 +12,10 @@
 // LDS, and rows of up to NCH*64*8*WPR elements stay in registers so the input
 // is read once.
 //
-// Exact division, cheaply. The quantized value must equal rint of the
-// correctly rounded binary32 quotient x / s. Per element we form
-// t = fl(x * r) with r = fl(1 / s) (one IEEE division per row); |x/s| <= 127
-// (1 + 2^-23), so |t - fl(x/s)| <= 127 * 1.5 * 2^-23 < 2^-15. When t is more
-// than 2^-14 away from the nearest half-integer, rint(t) == rint(fl(x/s)) and
-// t decides; otherwise (about 1 element in 8000) the element takes the full
-// IEEE division. Rows whose scale is subnormal (1/s would overflow) always
-// divide. The vLLM log's inverted-scale trick alone would not be exact: it
-// moves about one element per 4096-wide row across a rounding boundary.
-//
-// Rounding and the byte in one add: for |t| < 2^22, m = fl(t + 1.5 * 2^23)
-// rounds t to the nearest integer, ties to even, and the low byte of m's bit
-// pattern is that integer in two's complement. |t| <= 127 here, so the clamp
-// of the definition never binds on this path.
-#include "common.hpp"
+// The element arithmetic (exact division on multiplies, rounding, the byte)
+// is in quant_math.hpp.
 #include "launch.hpp"
+#include "quant_math.hpp"
 
 namespace w8a8 {
 namespace {
@@ -35,34 +23,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
 constexpr int kMaxRegChunks = 8;     // chunks of 8 elements held per lane
-constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-constexpr float kTieGuard = 0.5f - 0x1p-14f;
-
-// 8 consecutive inputs -> float (bf16 widening is exact), and their absmax
-// folded into `amax` (non-negative floats order like their bit patterns).
-__device__ __forceinline__ void load8(const uint16_t *p, float v[8], uint32_t &amax) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        v[2 * h] = bf16_lo(w[h]);
-        v[2 * h + 1] = bf16_hi(w[h]);
-        const uint32_t a = w[h] & 0x7FFF7FFFu;
-        const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
-        amax = max(amax, max(lo, hi) << 16);
-    }
-}
-
-__device__ __forceinline__ void load8(const float *p, float v[8], uint32_t &amax) {
-    const float4 a = reinterpret_cast<const float4 *>(p)[0];
-    const float4 b = reinterpret_cast<const float4 *>(p)[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    float m = __uint_as_float(amax);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
-    amax = __float_as_uint(m);
-}
 
 __device__ __forceinline__ uint32_t wave_max(uint32_t bits) {
 #pragma unroll
@@ -71,55 +31,6 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t bits) {
         bits = bits > o ? bits : o;
     }
     return bits;
-}
-
-struct RowScale {
-    float s;     // fl32(absmax / 127)
-    float r;     // fl32(1 / s) when fast
-    bool fast;   // s is a normal number: the reciprocal test applies
-};
-
-__device__ __forceinline__ RowScale row_scale(float absmax) {
-    RowScale rs;
-    rs.s = absmax / 127.0f;  // IEEE division
-    rs.fast = rs.s >= 0x1p-126f;
-    rs.r = rs.fast ? 1.0f / rs.s : 0.0f;
-    return rs;
-}
-
-// The byte of rint(fl(x / s)) clamped to [-127, 127], by IEEE division.
-__device__ __forceinline__ uint32_t quantize_div(float x, float s) {
-    if (s == 0.0f) return 0;
-    const float q = __builtin_fminf(__builtin_fmaxf(x / s, -127.0f), 127.0f);
-    return __float_as_uint(q + kMagic) & 0xFFu;
-}
-
-__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
-    return (b0 & 0xFFu) | ((b1 & 0xFFu) << 8) | ((b2 & 0xFFu) << 16) | (b3 << 24);
-}
-
-// 8 values -> 8 int8 codes (two packed words)
-__device__ __forceinline__ uint2 quantize8(const float v[8], const RowScale &rs) {
-    uint32_t b[8];
-    if (rs.fast) {
-        bool near_tie = false;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float t = v[e] * rs.r;
-            const float m = t + kMagic;
-            const float k = m - kMagic;  // rint(t), exact
-            near_tie |= __builtin_fabsf(t - k) >= kTieGuard;
-            b[e] = __float_as_uint(m);
-        }
-        if (near_tie) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) b[e] = quantize_div(v[e], rs.s);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) b[e] = quantize_div(v[e], rs.s);
-    }
-    return make_uint2(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]));
 }
 
 // Row m is handled by WPR consecutive wavefronts; wavefront w of the row takes

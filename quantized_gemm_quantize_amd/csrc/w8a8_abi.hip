@@ -119,6 +119,25 @@ w8a8_status w8a8_gemm_addmm(const int8_t *xq, const float *x_scale, int64_t M, c
                                         false, static_cast<hipStream_t>(stream), &am));
 }
 
+w8a8_status w8a8_fused_linear(const void *x_bf16, int64_t M, int64_t K, const int8_t *wq,
+                              const float *w_scale, int64_t N, const float *bias, float alpha,
+                              float beta, void *out, void *stream) {
+    if (M < 0 || M > W8A8_FUSED_MAX_M || N <= 0 || N % 16 != 0 || too_big(M, N))
+        return W8A8_ERR_SHAPE;
+    if (w8a8_status s = check_k(K)) return s;
+    if (!std::isfinite(alpha) || !std::isfinite(beta)) return W8A8_ERR_VALUE;
+    if (M == 0) return W8A8_OK;
+    if (!x_bf16 || !wq || !w_scale || !out) return W8A8_ERR_NULL;
+    if (!bias && beta != 0.0f) return W8A8_ERR_NULL;
+    if (misaligned(x_bf16) || misaligned(wq) || misaligned(w_scale) || misaligned(out) ||
+        (bias && misaligned(bias)))
+        return W8A8_ERR_ALIGN;
+    const w8a8::Addmm am{bias, alpha, beta};
+    return hip_status(w8a8::launch_linear_decode(static_cast<const uint16_t *>(x_bf16), (int)M, wq,
+                                                 w_scale, (int)N, (int)K, out,
+                                                 static_cast<hipStream_t>(stream), am));
+}
+
 w8a8_status w8a8_bsr_gemm(const int8_t *xq, const float *x_scale, int64_t M, int64_t K,
                           const int32_t *crow, const int32_t *col, const int8_t *values,
                           int64_t nnzb, int64_t bs, const float *w_scale, int64_t N, void *out,

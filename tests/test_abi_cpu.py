@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_gemm_addmm",
-               "w8a8_bsr_gemm", "w8a8_status_string", "w8a8_last_hip_error"):
+               "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_status_string",
+               "w8a8_last_hip_error"):
         assert fn in names
 
 
@@ -44,6 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert f"#define W8A8_MAX_K {binding.W8A8_MAX_K}" in text
+    assert f"#define W8A8_FUSED_MAX_M {binding.W8A8_FUSED_MAX_M}" in text
     assert 127 * 127 * binding.W8A8_MAX_K < 2 ** 31
     assert 127 * 127 * (binding.W8A8_MAX_K + 16) >= 2 ** 31
     for name in ("W8A8_ERR_NULL", "W8A8_ERR_SHAPE", "W8A8_ERR_ALIGN", "W8A8_ERR_K_OVERFLOW",
@@ -108,6 +110,27 @@ def test_gemm_addmm_validation(lib):
         assert g(*args(**{k: P + 4})) == ALIGN, k
     assert g(*args(bias=0, beta=0.0, M=0)) == OK        # no bias term, empty: no launch
     assert g(*args(M=0, xq=0, xs=0, out=0)) == OK
+
+
+def test_fused_linear_validation(lib):
+    f = lib.w8a8_fused_linear
+    args = lambda **kw: [kw.get("x", P), kw.get("M", 16), kw.get("K", 64), kw.get("wq", P),
+                         kw.get("ws", P), kw.get("N", 64), kw.get("bias", P),
+                         kw.get("alpha", 1.0), kw.get("beta", 1.0), kw.get("out", P), None]
+    assert f(*args(M=-1)) == SHAPE
+    assert f(*args(M=65)) == SHAPE                      # above W8A8_FUSED_MAX_M
+    assert f(*args(N=40)) == SHAPE
+    assert f(*args(N=0)) == SHAPE
+    assert f(*args(K=72)) == SHAPE
+    assert f(*args(K=0)) == SHAPE
+    assert f(*args(K=133152)) == KOVF
+    assert f(*args(alpha=float("inf"))) == VALUE
+    assert f(*args(beta=float("nan"))) == VALUE
+    for k in ("x", "wq", "ws", "out", "bias"):
+        assert f(*args(**{k: 0})) == NULL, k
+        assert f(*args(**{k: P + 2})) == ALIGN, k
+    assert f(*args(bias=0, beta=0.0, M=0)) == OK        # no bias term, empty: no launch
+    assert f(*args(M=0, x=0, out=0)) == OK
 
 
 def test_bsr_validation(lib):

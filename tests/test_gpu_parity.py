@@ -281,6 +281,100 @@ def test_gemm_addmm_identity_is_the_plain_gemm(b, oracle):
         assert torch.equal(plain.view(torch.int16), am.view(torch.int16)), M
 
 
+# --- fused single-launch linear (M <= 64) ------------------------------------
+
+def _fused_case(b, oracle, x_bits, w, alpha=1.0, beta=0.0, bias=None, what=""):
+    """w8a8_fused_linear against the oracle's quantize -> int GEMM -> epilogue, and bit for bit
+    against the two-launch GPU path (quantize_rows, then the GEMM) on the same inputs."""
+    x = to_dev_bf16(x_bits)
+    wq, sw, wq_ref, sw_ref = gpu_weights(b, oracle, w)
+    bias_dev = None if bias is None else torch.from_numpy(bias).to(DEV)
+    got = bf16_bits(b.w8a8_fused_linear(x, wq, sw, bias=bias_dev, alpha=alpha, beta=beta))
+    xq_ref, sx_ref = oracle.quantize_rows_bf16(x_bits)
+    acc = oracle.gemm_i32(xq_ref, wq_ref)
+    plain = alpha == 1.0 and bias is None
+    if plain:
+        assert_bf16_close(got, oracle.epilogue_bf16(acc, sx_ref, sw_ref), what)
+    else:
+        ref = oracle.epilogue_addmm_bf16(acc, sx_ref, sw_ref, bias, alpha, beta)
+        g = bf16_bits_to_f32(got).astype(np.float64)
+        o = bf16_bits_to_f32(ref).astype(np.float64)
+        t = acc.astype(np.float64) * sx_ref.astype(np.float64)[:, None] * sw_ref.astype(np.float64)[None, :]
+        mag = np.abs(alpha * t)
+        if bias is not None:
+            mag = mag + np.abs(beta * bias.astype(np.float64))[None, :]
+        bound = _bf16_ulp(np.maximum(np.abs(g), np.abs(o))) + mag * 2.0 ** -20
+        assert (np.abs(g - o) <= bound).all(), (what, np.max(np.abs(g - o) - bound))
+    xq, sx = b.w8a8_quantize_rows(x)
+    two = b.w8a8_gemm(xq, sx, wq, sw) if plain else b.w8a8_gemm_addmm(
+        xq, sx, wq, sw, bias=bias_dev, alpha=alpha, beta=beta)
+    assert np.array_equal(got, bf16_bits(two)), f"{what}: fused differs from quantize + GEMM"
+    return got
+
+
+FUSED_SHAPES = [
+    (1, 16, 16), (1, 64, 64), (5, 48, 80), (3, 1040, 16), (16, 128, 4096), (16, 256, 4112),
+    (17, 64, 4112), (31, 96, 1040), (33, 32, 192), (48, 160, 528), (64, 96, 512), (64, 256, 8192),
+    (7, 32, 16400),
+]
+
+
+@pytest.mark.parametrize("M,N,K", FUSED_SHAPES)
+def test_fused_linear_shapes(b, oracle, M, N, K):
+    log(f"fused linear M={M} N={N} K={K}")
+    inp = make_linear(M, N, K, seed=M * 5 + N + 3 * K)
+    _fused_case(b, oracle, inp.x_bits, inp.w, what=f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (16, 256, 512), (40, 128, 4096), (64, 512, 320)])
+@pytest.mark.parametrize("alpha,beta,with_bias", [(1.0, 1.0, True), (0.5, -2.0, True),
+                                                  (-1.25, 0.0, True), (2.0, 0.0, False)])
+def test_fused_linear_addmm(b, oracle, M, N, K, alpha, beta, with_bias):
+    log(f"fused linear addmm M={M} N={N} K={K} alpha={alpha} beta={beta} bias={with_bias}")
+    inp = make_linear(M, N, K, seed=M + N + K + 11)
+    rng = np.random.default_rng(M * 3 + N)
+    bias = (rng.standard_normal(N) * 0.5).astype(np.float32) if with_bias else None
+    _fused_case(b, oracle, inp.x_bits, inp.w, alpha, beta, bias, f"M={M} N={N} K={K}")
+
+
+def test_fused_linear_special_rows(b, oracle):
+    """Zero, subnormal, huge, constant and near-tie rows quantized inside the GEMM."""
+    log("fused linear special rows")
+    from quantized_gemm_quantize_amd.inputs import f32_to_bf16_bits
+    K, N = 256, 64
+    rng = np.random.default_rng(5)
+    rows = np.zeros((40, K), np.float32)
+    rows[1] = rng.standard_normal(K) * 2.0 ** -130
+    rows[2] = rng.standard_normal(K) * 1e-38
+    rows[3] = rng.standard_normal(K) * 1e30
+    rows[4, 0], rows[4, 1:] = 4.5, -2.25
+    rows[5] = np.float32(-3.0)
+    rows[6:38, 0] = 2.0 + np.arange(32) / 16.0                # x = absmax / 2 family
+    rows[6:38, 1:] = (rows[6:38, 0] / 2)[:, None]
+    rows[38] = rng.standard_normal(K)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    got = _fused_case(b, oracle, f32_to_bf16_bits(rows), w, what="special rows")
+    assert (got[0] == 0).all() and (got[39] == 0).all()      # all-zero rows give +0
+
+
+def test_fused_linear_decode_workload_full_size(b, oracle):
+    name = "decode"
+    log(f"fused linear workload {name} {CONFIGS[name]}")
+    inp = make_inputs(name)
+    _fused_case(b, oracle, inp.x_bits, inp.w, what=name)
+
+
+def test_fused_linear_limits(b):
+    wq = torch.zeros((32, 64), dtype=torch.int8, device=DEV)
+    ws = torch.ones((32,), dtype=torch.float32, device=DEV)
+    out = b.w8a8_fused_linear(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV), wq, ws,
+                              beta=0.0)
+    assert out.shape == (0, 32)
+    with pytest.raises(b.W8A8Error):
+        b.w8a8_fused_linear(torch.zeros((65, 64), dtype=torch.bfloat16, device=DEV), wq, ws,
+                            beta=0.0)
+
+
 # --- block-sparse GEMM ------------------------------------------------------
 
 def _bsr_case(b, oracle, M, N, K, zero_frac, seed, rows=None):
