@@ -7,6 +7,8 @@ from .oracle import (  # noqa: F401
     build_oracle,
     bf16_rne_from_f64,
     bsr_gemm_i32,
+    compress24,
+    decompress24,
     epilogue_addmm_bf16,
     epilogue_bf16,
     gemm_i32,

@@ -55,6 +55,10 @@ def load_oracle():
     lib.oracle_epilogue_addmm_bf16.restype = None
     lib.oracle_bsr_gemm_i32.argtypes = [p, i64, i64, p, p, p, i64, i64, p]
     lib.oracle_bsr_gemm_i32.restype = ctypes.c_int
+    lib.oracle_compress24.argtypes = [p, i64, i64, p, p]
+    lib.oracle_compress24.restype = None
+    lib.oracle_decompress24.argtypes = [p, p, i64, i64, p]
+    lib.oracle_decompress24.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -164,6 +168,33 @@ def bsr_gemm_i32(xq: np.ndarray, crow: np.ndarray, col: np.ndarray, values: np.n
     if rc != 0:
         raise OverflowError("int8 dot product leaves the int32 range")
     return acc
+
+
+def compress24(w: np.ndarray):
+    """int8 [N,K] (K % 64 == 0) -> (values int8 [N,K/2], meta uint32 [N,K/32]): the two
+    largest magnitudes of each group of 4 along K, in the library's storage order."""
+    w = _c(w, np.int8)
+    N, K = w.shape
+    if K % 64:
+        raise ValueError("K must be a multiple of 64")
+    values = np.empty((N, K // 2), np.int8)
+    meta = np.empty((N, K // 32), np.uint32)
+    load_oracle().oracle_compress24(_ptr(w), N, K, _ptr(values), _ptr(meta))
+    return values, meta
+
+
+def decompress24(values: np.ndarray, meta: np.ndarray) -> np.ndarray:
+    """The dense int8 [N,K] weight that compressed 2:4 arrays hold."""
+    values = _c(values, np.int8)
+    meta = _c(meta, np.uint32)
+    N, K2 = values.shape
+    K = 2 * K2
+    if K % 64 or meta.shape != (N, K // 32):
+        raise ValueError("2:4 array shapes")
+    w = np.empty((N, K), np.int8)
+    if load_oracle().oracle_decompress24(_ptr(values), _ptr(meta), N, K, _ptr(w)) != 0:
+        raise ValueError("a group's positions are not p0 < p1")
+    return w
 
 
 def num_threads() -> int:

@@ -42,6 +42,13 @@
  *                (crow_indices / col_indices / values), pytorch/ao PR #821
  *                custom-op paragraph and the bsr_dense_addmm warning (Ms=64,
  *                Ks=64, beta=0, alpha=1).
+ *   2:4 weights: in every group of 4 consecutive weights along K at most two
+ *                are kept -- the pages' cuSPARSELt route (Paddle PR #41770:
+ *                sparse_fc on FC weights already pruned to 2:4, the
+ *                "sparse_2_4" pass; pytorch/ao PR #821: the 2:4 path and its
+ *                i8i8 -> bf16 output). The product is the dense int8 GEMM of
+ *                the decompressed weight; the compressed storage is the
+ *                library's own (see oracle_compress24).
  */
 #include <math.h>
 #include <stdint.h>
@@ -203,6 +210,80 @@ int oracle_bsr_gemm_i32(const int8_t *xq, int64_t M, int64_t K, const int32_t *c
                 }
                 if (sum > INT32_MAX || sum < INT32_MIN) bad = 1;
                 acc[m * N + r * bs + i] = (int32_t)sum;
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * 2:4 compression of an int8 weight w [N,K] (K % 64 == 0).
+ *
+ * Group g of row n is w[n][4g .. 4g+3]. Its kept positions p0 < p1 are the two
+ * largest |w| of the group, equal magnitudes taken in position order (the
+ * pages take weights that are already 2:4; with at most two nonzeros in a
+ * group this keeps all of them, so such a weight is stored exactly).
+ *
+ * Storage, per row n and 64-column step s (groups 16s .. 16s+15): the groups
+ * are listed in the order 0,1,2,3, 8,9,10,11, 4,5,6,7, 12,13,14,15 of the step,
+ * list position c holding group 16s + order[c];
+ *   values[n][32s + 2c + t] = w[n][4 (16s + order[c]) + p_t]      (t = 0, 1)
+ *   meta[n][2s + c/8], bits 4 (c%8) .. 4 (c%8) + 3 = p0 | p1 << 2
+ * values is int8 [N, K/2], meta uint32 [N, K/32].
+ */
+static const int kGroupOrder24[16] = {0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15};
+
+static int abs_i8(int8_t v) { return v < 0 ? -(int)v : (int)v; }
+
+/* The two kept positions of one group of 4, p0 < p1. */
+static void kept_pair24(const int8_t *grp, int *p0, int *p1) {
+    int first = 0;
+    for (int p = 1; p < 4; ++p)
+        if (abs_i8(grp[p]) > abs_i8(grp[first])) first = p;
+    int second = -1;
+    for (int p = 0; p < 4; ++p) {
+        if (p == first) continue;
+        if (second < 0 || abs_i8(grp[p]) > abs_i8(grp[second])) second = p;
+    }
+    *p0 = first < second ? first : second;
+    *p1 = first < second ? second : first;
+}
+
+void oracle_compress24(const int8_t *w, int64_t N, int64_t K, int8_t *values, uint32_t *meta) {
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t s = 0; s < K / 64; ++s) {
+            uint32_t words[2] = {0, 0};
+            for (int c = 0; c < 16; ++c) {
+                const int8_t *grp = w + n * K + 4 * (16 * s + kGroupOrder24[c]);
+                int p0, p1;
+                kept_pair24(grp, &p0, &p1);
+                values[n * (K / 2) + 32 * s + 2 * c] = grp[p0];
+                values[n * (K / 2) + 32 * s + 2 * c + 1] = grp[p1];
+                words[c / 8] |= (uint32_t)(p0 | (p1 << 2)) << (4 * (c % 8));
+            }
+            meta[n * (K / 32) + 2 * s] = words[0];
+            meta[n * (K / 32) + 2 * s + 1] = words[1];
+        }
+    }
+}
+
+/* The inverse: w [N,K] with the stored values at their positions, zeros
+ * elsewhere. Returns 0, or -1 if a group's two positions are not p0 < p1. */
+int oracle_decompress24(const int8_t *values, const uint32_t *meta, int64_t N, int64_t K,
+                        int8_t *w) {
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) w[n * K + k] = 0;
+        for (int64_t s = 0; s < K / 64; ++s) {
+            for (int c = 0; c < 16; ++c) {
+                const uint32_t nib = (meta[n * (K / 32) + 2 * s + c / 8] >> (4 * (c % 8))) & 15u;
+                const int p0 = (int)(nib & 3u), p1 = (int)(nib >> 2);
+                if (!(p0 < p1)) bad = 1;
+                int8_t *grp = w + n * K + 4 * (16 * s + kGroupOrder24[c]);
+                grp[p0] = values[n * (K / 2) + 32 * s + 2 * c];
+                grp[p1] = values[n * (K / 2) + 32 * s + 2 * c + 1];
             }
         }
     }

@@ -18,9 +18,15 @@ Workloads (shapes of the pages' examples):
   bsr_fc2           X [16448,5120], W [1280,5120] as 64x64 blocks with 80% of the
                     blocks zero (the ViT-H MLP fc2 shape of the same warning, at
                     the 0.8 linear sparsity of that benchmark command)
+  sparse24          the prefill_outliers layer with a 2:4 weight: in every group
+                    of 4 consecutive weights along K two are zero (the
+                    semi-structured pattern of the pages' cuSPARSELt route)
+  sparse24_decode   the decode layer with a 2:4 weight
 
 Draw order from numpy.random.default_rng(seed) (PCG64): X ~ N(0,1) float32,
-then the outlier channels, then W = 0.02 * N(0,1) float32, then the block mask.
+then the outlier channels, then W = 0.02 * N(0,1) float32, then the block mask,
+then the 2:4 pattern (one of the 6 pairs of kept positions per group of 4,
+uniform).
 """
 from __future__ import annotations
 
@@ -36,10 +42,17 @@ CONFIGS = {
     "large_m": dict(M=38400, K=1024, N=4096),
     "bsr": dict(M=16448, K=1280, N=5120, bs=64, zero_frac=0.9),
     "bsr_fc2": dict(M=16448, K=5120, N=1280, bs=64, zero_frac=0.8),
+    "sparse24": dict(M=2048, K=4096, N=4096, outlier_frac=0.01, outlier_scale=20.0,
+                     sparse24=True),
+    "sparse24_decode": dict(M=16, K=4096, N=4096, sparse24=True),
 }
 
 # Order of the configurations as the workload list states them.
-CONFIG_ORDER = ["tiny", "decode", "prefill_outliers", "large_m", "bsr", "bsr_fc2"]
+CONFIG_ORDER = ["tiny", "decode", "prefill_outliers", "large_m", "bsr", "bsr_fc2", "sparse24",
+                "sparse24_decode"]
+
+# The 6 ways to keep 2 of 4 positions, as (p0, p1) with p0 < p1.
+PAIRS_24 = [(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)]
 
 
 @dataclass
@@ -84,12 +97,13 @@ def make_inputs(name: str, seed: int = 0, M: int | None = None) -> LinearInputs:
     return make_linear(cfg["M"], cfg["N"], cfg["K"], seed=seed,
                        outlier_frac=cfg.get("outlier_frac", 0.0),
                        outlier_scale=cfg.get("outlier_scale", 1.0),
-                       bs=cfg.get("bs", 0), zero_frac=cfg.get("zero_frac", 0.0), name=name)
+                       bs=cfg.get("bs", 0), zero_frac=cfg.get("zero_frac", 0.0),
+                       sparse24=cfg.get("sparse24", False), name=name)
 
 
 def make_linear(M: int, N: int, K: int, seed: int = 0, outlier_frac: float = 0.0,
                 outlier_scale: float = 1.0, bs: int = 0, zero_frac: float = 0.0,
-                name: str = "random") -> LinearInputs:
+                sparse24: bool = False, name: str = "random") -> LinearInputs:
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((M, K), dtype=np.float32)
     meta = {"seed": seed, "numpy": np.__version__}
@@ -111,6 +125,14 @@ def make_linear(M: int, N: int, K: int, seed: int = 0, outlier_frac: float = 0.0
         dense_mask = np.repeat(np.repeat(mask, bs, axis=0), bs, axis=1)
         w = np.where(dense_mask, w, np.float32(0.0)).astype(np.float32)
         meta["nnzb"] = int(n_keep)
+    if sparse24:
+        assert K % 4 == 0
+        pattern = rng.integers(0, len(PAIRS_24), size=(N, K // 4))
+        keep = np.zeros((len(PAIRS_24), 4), dtype=bool)
+        for i, (p0, p1) in enumerate(PAIRS_24):
+            keep[i, [p0, p1]] = True
+        w = np.where(keep[pattern].reshape(N, K), w, np.float32(0.0)).astype(np.float32)
+        meta["sparse24"] = True
     return LinearInputs(name=name, x_bits=f32_to_bf16_bits(x), w=w, block_mask=mask, bs=bs,
                         meta=meta)
 

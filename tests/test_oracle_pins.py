@@ -342,3 +342,73 @@ def test_prefill_outlier_channels():
     # seeded: the same draw twice
     assert np.array_equal(make_inputs("prefill_outliers", M=64).x_bits, inp.x_bits)
     assert torch.bfloat16 is not None
+
+
+# --- 2:4 semi-structured weights --------------------------------------------
+
+def test_compress24_hand_worked_row(oracle):
+    """The storage of one 2:4 row, worked by hand from its definition."""
+    g = _load("sparse24_row.json")
+    row = np.zeros(64, np.int8)
+    for grp in range(16):
+        p0, p1 = g["pairs"][grp % 6]
+        row[4 * grp + p0] = grp + 1
+        row[4 * grp + p1] = -(grp + 1)
+    values, meta = oracle.compress24(row[None, :])
+    assert values[0].tolist() == g["values"]
+    assert [int(m) for m in meta[0]] == [int(h, 16) for h in g["meta"]]
+    assert np.array_equal(oracle.decompress24(values, meta)[0], row)
+
+
+def _brute_force_prune24(w: np.ndarray) -> np.ndarray:
+    """Keep the two largest |w| of each group of 4 (equal magnitudes in position order)."""
+    N, K = w.shape
+    out = np.zeros_like(w)
+    for n in range(N):
+        for g in range(K // 4):
+            grp = [int(v) for v in w[n, 4 * g:4 * g + 4]]
+            order = sorted(range(4), key=lambda p: (-abs(grp[p]), p))
+            for p in order[:2]:
+                out[n, 4 * g + p] = grp[p]
+    return out
+
+
+def test_compress24_keeps_the_two_largest_magnitudes(oracle):
+    """On a dense int8 matrix the stored weight is the brute-force top-2 selection, ties
+    included (small value range so that equal magnitudes are frequent)."""
+    rng = np.random.default_rng(24)
+    w = rng.integers(-3, 4, size=(9, 192), dtype=np.int8)
+    w[0, :8] = -128                                   # int8 extremes
+    w[1, :8] = 127
+    values, meta = oracle.compress24(w)
+    assert np.array_equal(oracle.decompress24(values, meta), _brute_force_prune24(w))
+
+
+def test_compress24_is_lossless_on_2to4_weights(oracle):
+    """The generator's 2:4 weights, quantized per channel, survive the round trip, and every
+    nibble lists two distinct positions in increasing order."""
+    inp = make_linear(8, 64, 256, seed=7, sparse24=True)
+    wq, _ = oracle.quantize_rows_f32(inp.w)
+    assert ((wq.reshape(64, -1, 4) != 0).sum(-1) <= 2).all()
+    values, meta = oracle.compress24(wq)
+    assert np.array_equal(oracle.decompress24(values, meta), wq)
+    nib = (meta[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 15
+    assert ((nib & 3) < (nib >> 2)).all()
+
+
+def test_decompress24_rejects_bad_positions(oracle):
+    values = np.zeros((1, 32), np.int8)
+    meta = np.array([[0x44444444, 0x44444441]], np.uint32)   # last nibble: p0 = 1, p1 = 0
+    with pytest.raises(ValueError):
+        oracle.decompress24(values, meta)
+
+
+def test_sparse24_product_matches_float64_matmul(oracle):
+    """The 2:4 product (dense GEMM of the decompressed weight) against a float64 matmul of
+    the original 2:4 int8 weight."""
+    inp = make_linear(5, 32, 128, seed=3, sparse24=True)
+    xq, _ = oracle.quantize_rows_bf16(inp.x_bits)
+    wq, _ = oracle.quantize_rows_f32(inp.w)
+    acc = oracle.gemm_i32(xq, oracle.decompress24(*oracle.compress24(wq)))
+    ref = xq.astype(np.float64) @ wq.astype(np.float64).T
+    assert np.array_equal(acc.astype(np.float64), ref)
