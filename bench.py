@@ -54,7 +54,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="prefill_outliers",
-                    choices=["tiny", "decode", "prefill_outliers", "large_m", "bsr", "bsr_fc2"])
+                    choices=["tiny", "decode", "prefill_outliers", "large_m", "bsr", "bsr_fc2",
+                             "sparse24", "sparse24_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -138,6 +139,8 @@ def prepare(name: str, torch, np, b, dev):
     x = torch.from_numpy(inp.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     wq, sw = b.w8a8_quantize_rows_f32(torch.from_numpy(inp.w).to(dev))
     d = dict(inp=inp, x=x, wq=wq, sw=sw)
+    if inp.meta.get("sparse24"):
+        d["values24"], d["meta24"] = b.w8a8_compress24(wq)
     if inp.bs:
         crow, col, values = bsr_from_dense(wq.cpu().numpy(), inp.block_mask, inp.bs)
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -154,10 +157,14 @@ def cpu_baseline(name: str, np):
     M, N, K = inp.M, inp.N, inp.K
     bsr = bsr_from_dense(wq, inp.block_mask, inp.bs) if inp.bs else None
 
+    sparse24 = oracle.compress24(wq) if inp.meta.get("sparse24") else None
+
     def run(rows):
         t0 = time.perf_counter()
         xq, sx = oracle.quantize_rows_bf16(inp.x_bits[:rows])
-        if bsr is None:
+        if sparse24 is not None:
+            acc = oracle.gemm_i32(xq, oracle.decompress24(*sparse24))
+        elif bsr is None:
             acc = oracle.gemm_i32(xq, wq)
         else:
             acc = oracle.bsr_gemm_i32(xq, *bsr, N)
@@ -169,10 +176,14 @@ def cpu_baseline(name: str, np):
     rows = int(min(M, max(probe, probe * 15.0 / max(t_probe, 1e-6))))
     t = run(rows)
     ops = 2.0 * rows * N * K
+    if sparse24 is not None:
+        ops /= 2          # the kept products only, as the GPU line counts them
     return {"value": round(ops / t / 1e12, 6), "unit": "TOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of the {name} workload (M={M}, N={N}, K={K}): "
-                      f"quantize + exact int GEMM + float64 epilogue, {t:.2f} s wall"}
+                      f"quantize + exact int GEMM + float64 epilogue"
+                      + (" (2:4 weight decompressed inside the timed region)" if sparse24 else "")
+                      + f", {t:.2f} s wall"}
 
 
 def bench_decode(torch, np, b, dev, steps, warmup, eager=False):
@@ -244,13 +255,22 @@ def main():
     inp = d["inp"]
     M, N, K = inp.M, inp.N, inp.K
     bsr = bool(inp.bs)
+    sp24 = "values24" in d
 
     # rotated input sets: X, weights and outputs at distinct addresses
-    per_set = 2 * M * K + M * K + (len(d["values"].view(-1)) if bsr else N * K) + 2 * M * N
+    if bsr:
+        w_bytes = d["values"].numel()
+    elif sp24:
+        w_bytes = N * K // 2 + N * K // 8
+    else:
+        w_bytes = N * K
+    per_set = 2 * M * K + M * K + w_bytes + 2 * M * N
     R = rotation(per_set)
     xs = [d["x"].clone() for _ in range(R)]
     if bsr:
         ws = [d["values"].clone() for _ in range(R)]
+    elif sp24:
+        ws = [(d["values24"].clone(), d["meta24"].clone()) for _ in range(R)]
     else:
         ws = [d["wq"].clone() for _ in range(R)]
     xqs = [torch.empty((M, K), dtype=torch.int8, device=dev) for _ in range(R)]
@@ -265,6 +285,8 @@ def main():
         j = i % R
         if bsr:
             b.w8a8_bsr_gemm(xqs[j], sxs[j], d["crow"], d["col"], ws[j], d["sw"], out=outs[j])
+        elif sp24:
+            b.w8a8_sparse24_gemm(xqs[j], sxs[j], ws[j][0], ws[j][1], d["sw"], out=outs[j])
         else:
             b.w8a8_gemm(xqs[j], sxs[j], ws[j], d["sw"], out=outs[j])
 
@@ -288,6 +310,9 @@ def main():
     if bsr:
         # stored blocks only: each 64x64 block is a 64-deep product for all M rows
         ops = 2.0 * M * 64 * 64 * int(d["values"].shape[0])
+    elif sp24:
+        # the kept products only: two of every four weights
+        ops = 1.0 * M * N * K
     value = ops / (ms_step * 1e-3) / 1e12
     gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
     q_bytes = 2 * M * K + M * K + 4 * M
@@ -300,7 +325,6 @@ def main():
 
     if bsr or M <= 64:
         # HBM bound: the BSR output write, or the M <= 64 weight stream
-        w_bytes = d["values"].numel() if bsr else N * K
         gemm_bytes = M * K + 4 * M + w_bytes + 4 * N + 2 * M * N
         roof = {"bound": "hbm", "achieved": round(gemm_bytes / (ms_gemm * 1e-3) / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -309,7 +333,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS,
                 "unit": "TOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4)}
     roof["traffic"] = traffic
-    roof["kernel"] = "w8a8_bsr_gemm" if bsr else "w8a8_gemm"
+    kernel = "w8a8_bsr_gemm" if bsr else "w8a8_sparse24_gemm" if sp24 else "w8a8_gemm"
+    roof["kernel"] = kernel
     roof["avg_launch_us"] = round(ms_gemm * 1e3, 3)
 
     line = {
@@ -326,8 +351,10 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "timing": "eager launches" if args.eager else "HIP graph replay",
-        "config": {"workload": f"{name} M={M} K={K} N={N}" + (f" BSR 64x64 nnzb={d['values'].shape[0]}" if bsr else ""),
-                   "step": "w8a8_quantize_rows + " + ("w8a8_bsr_gemm" if bsr else "w8a8_gemm"),
+        "config": {"workload": f"{name} M={M} K={K} N={N}"
+                   + (f" BSR 64x64 nnzb={d['values'].shape[0]}" if bsr else "")
+                   + (" 2:4 weight (ops: kept products, M*N*K)" if sp24 else ""),
+                   "step": "w8a8_quantize_rows + " + kernel,
                    "seed": 0, "input_sets_rotated": R},
         "roofline": roof,
         "quantize_rows": {"us": round(ms_quant * 1e3, 3),
@@ -336,6 +363,8 @@ def main():
         "gemm_only": {"us": round(ms_gemm * 1e3, 3), "TOPs": round(gemm_tops, 1),
                       "frac_of_int8_peak": round(gemm_tops / PEAK_INT8_TOPS, 4)},
     }
+    if sp24:
+        line["gemm_only"]["dense_equivalent_TOPs"] = round(2 * gemm_tops, 1)
     if not args.no_decode and name == "prefill_outliers":
         line["decode_m16"] = bench_decode(torch, np, b, dev, args.steps, args.warmup, args.eager)
     if not args.no_cpu_baseline:

@@ -58,8 +58,10 @@ def load():
     f32 = ctypes.c_float
     lib.w8a8_gemm_addmm.argtypes = [p, p, i64, p, p, i64, i64, p, f32, f32, p, p]
     lib.w8a8_fused_linear.argtypes = [p, i64, i64, p, p, i64, p, f32, f32, p, p]
+    lib.w8a8_compress24.argtypes = [p, i64, i64, p, p, p]
+    lib.w8a8_sparse24_gemm.argtypes = [p, p, i64, p, p, p, i64, i64, p, i32, p]
     for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_gemm_addmm",
-               "w8a8_fused_linear", "w8a8_bsr_gemm"):
+               "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_compress24", "w8a8_sparse24_gemm"):
         getattr(lib, fn).restype = i32
     lib.w8a8_status_string.argtypes = [i32]
     lib.w8a8_status_string.restype = ctypes.c_char_p
@@ -173,6 +175,44 @@ def w8a8_gemm_addmm(xq, x_scale, wq, w_scale, bias=None, alpha=1.0, beta=1.0, ou
     _call("w8a8_gemm_addmm", xq.data_ptr(), x_scale.data_ptr(), M, wq.data_ptr(),
           w_scale.data_ptr(), N, K, None if bias is None else bias.data_ptr(), float(alpha),
           float(beta), out.data_ptr(), _stream_handle(stream))
+    return out
+
+
+def w8a8_compress24(wq, values=None, meta=None, stream=None):
+    """int8 [N,K] weight -> (values int8 [N,K/2], meta int32 [N,K/32] holding the uint32
+    index words): the 2:4 storage of include/w8a8.h (two largest |w| per group of 4)."""
+    _check_tensor(wq, "wq", torch.int8, 2)
+    N, K = wq.shape
+    if values is None:
+        values = torch.empty((N, K // 2), dtype=torch.int8, device=wq.device)
+    if meta is None:
+        meta = torch.empty((N, K // 32), dtype=torch.int32, device=wq.device)
+    _check_tensor(values, "values", torch.int8, 2)
+    _check_tensor(meta, "meta", torch.int32, 2)
+    if tuple(values.shape) != (N, K // 2) or tuple(meta.shape) != (N, K // 32):
+        raise ValueError("2:4 array shapes")
+    _call("w8a8_compress24", wq.data_ptr(), N, K, values.data_ptr(), meta.data_ptr(),
+          _stream_handle(stream))
+    return values, meta
+
+
+def w8a8_sparse24_gemm(xq, x_scale, values, meta, w_scale, out=None, out_dtype="bf16",
+                       stream=None):
+    """W8A8 GEMM on a compressed 2:4 weight (values [N,K/2] int8, meta [N,K/32] int32)."""
+    od = _out_dtype(out_dtype)
+    _check_tensor(xq, "xq", torch.int8, 2)
+    _check_tensor(x_scale, "x_scale", torch.float32, 1)
+    _check_tensor(values, "values", torch.int8, 2)
+    _check_tensor(meta, "meta", torch.int32, 2)
+    _check_tensor(w_scale, "w_scale", torch.float32, 1)
+    M, K = xq.shape
+    N = w_scale.shape[0]
+    if (tuple(values.shape) != (N, K // 2) or tuple(meta.shape) != (N, K // 32)
+            or tuple(x_scale.shape) != (M,)):
+        raise ValueError("operand shapes")
+    out = _out(out, M, N, od, xq.device)
+    _call("w8a8_sparse24_gemm", xq.data_ptr(), x_scale.data_ptr(), M, values.data_ptr(),
+          meta.data_ptr(), w_scale.data_ptr(), N, K, out.data_ptr(), od, _stream_handle(stream))
     return out
 
 

@@ -26,6 +26,14 @@ hipError_t launch_gemm(const int8_t *xq, const float *xs, int M, const int8_t *w
 hipError_t launch_linear_decode(const uint16_t *x, int M, const int8_t *wq, const float *ws, int N,
                                 int K, void *out, hipStream_t stream, const Addmm &am);
 
+// 2:4 weights: compression of an int8 [N,K] weight (K % 64 == 0) into values
+// [N,K/2] and meta [N,K/32], and the GEMM on the compressed weight.
+hipError_t launch_compress24(const int8_t *wq, int N, int K, int8_t *values, uint32_t *meta,
+                             hipStream_t stream);
+hipError_t launch_sparse24_gemm(const int8_t *xq, const float *xs, int M, const int8_t *values,
+                                const uint32_t *meta, const float *ws, int N, int K, void *out,
+                                bool out_i32, hipStream_t stream);
+
 // Compute units of the current device (queried once per device).
 int device_cu_count();
 

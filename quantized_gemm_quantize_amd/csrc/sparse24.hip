@@ -1,0 +1,439 @@
+// 2:4 semi-structured int8 weights on gfx950's sparse MFMA.
+//
+// In every group of 4 consecutive weights along K at most two are nonzero (the
+// pages' cuSPARSELt route: Paddle sparse_fc PR #41770 runs FC weights already
+// pruned to 2:4; pytorch/ao PR #821 composes that path with int8 dynamic
+// quantization and asks for i8i8 -> bf16 output so the int32 product is never
+// materialized). The sparse MFMA multiplies a 2:4 operand stored compressed --
+// two values and two 2-bit positions per group -- at twice the dense rate.
+//
+// Storage (the library's own, see include/w8a8.h): per weight row and 64-column
+// step the 16 groups are listed in the order 0-3, 8-11, 4-7, 12-15; values hold
+// the two kept weights of each listed group (lower position first), meta one
+// nibble p0 | p1 << 2 per listed group, eight per 32-bit word. That order is
+// the sparse operand's lane layout: for v_smfmac_i32_32x32x64_i8, lane half h
+// of weight row n takes the 16 value bytes and the index word of list half h
+// of the step (groups 4h..4h+3 and 8+4h..8+4h+3), against activation bytes
+// [32h, 32h+32) of the step in the other operand; v_smfmac_i32_16x16x128_i8
+// takes, in lane quarter q, list half q / 2 of 64-column step q % 2 against
+// activation bytes [32q, 32q+32) of its 128 columns. So every operand fragment
+// is one contiguous 16-byte load plus one 32-bit index.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace w8a8 {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v4i smfmac_16x16x128(v4i a, v8i b, v4i c, int idx) {
+    return __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, c, idx, 0, 0);
+}
+
+__device__ __forceinline__ int mag(int v) { return v < 0 ? -v : v; }
+
+// The group's kept positions p0 < p1 as the nibble p0 | p1 << 2, and its kept
+// values (lower position first) packed in the low 16 bits: the two largest
+// |w|, equal magnitudes in position order.
+__device__ __forceinline__ void keep_two(uint32_t grp, uint32_t &nib, uint32_t &vals) {
+    int w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) w[p] = (int)(int8_t)(grp >> (8 * p));
+    int first = 0;
+#pragma unroll
+    for (int p = 1; p < 4; ++p)
+        if (mag(w[p]) > mag(w[first])) first = p;
+    int second = first == 0 ? 1 : 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        if (p != first && p > second && mag(w[p]) > mag(w[second])) second = p;
+    const int p0 = min(first, second), p1 = max(first, second);
+    nib = (uint32_t)(p0 | (p1 << 2));
+    vals = ((uint32_t)w[p0] & 0xFFu) | (((uint32_t)w[p1] & 0xFFu) << 8);
+}
+
+// One thread per (row, 64-column step, list half): reads the 32 weights of its
+// 8 groups (columns [16h, 16h+16) and [32+16h, 32+16h+16) of the step), writes
+// 16 value bytes and one index word.
+__global__ __launch_bounds__(256) void compress24_kernel(const int8_t *__restrict__ w,
+                                                          int64_t chunks, int K,
+                                                          int8_t *__restrict__ values,
+                                                          uint32_t *__restrict__ meta) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= chunks) return;
+    const int per_row = K / 32;  // two chunks per 64-column step
+    const int64_t n = t / per_row;
+    const int c = (int)(t % per_row), s = c >> 1, h = c & 1;
+    const int8_t *row = w + n * K + 64 * s + 16 * h;
+    const uint4 lo = *reinterpret_cast<const uint4 *>(row);        // groups 4h .. 4h+3
+    const uint4 hi = *reinterpret_cast<const uint4 *>(row + 32);   // groups 8+4h .. 8+4h+3
+    const uint32_t grp[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint32_t word = 0, v[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t nib, vals;
+        keep_two(grp[i], nib, vals);
+        word |= nib << (4 * i);
+        v[i >> 1] |= vals << (16 * (i & 1));
+    }
+    *reinterpret_cast<uint4 *>(values + n * (K / 2) + 32 * s + 16 * h) = make_uint4(v[0], v[1], v[2], v[3]);
+    meta[n * per_row + c] = word;
+}
+
+// Weight-streaming 2:4 GEMM for M <= 64: the shape of the dense M-small kernel
+// (one workgroup per 16 output channels, K split over 8 wavefronts, partials
+// summed in LDS, fused epilogue), with v_smfmac_i32_16x16x128_i8 taking the
+// compressed weights as its sparse operand: half the weight bytes of the dense
+// kernel per output. The weight operand comes first, so lane l ends with
+// output channels 4 (l / 16) .. +3 of activation row l % 16.
+constexpr int kSplit = 8;
+constexpr int kUnroll = 4;   // 128-column steps whose loads are issued together
+
+template <int MT, bool OUT_I32>
+__global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_kernel(
+    const int8_t *__restrict__ X, const float *__restrict__ sx, const int8_t *__restrict__ V,
+    const uint32_t *__restrict__ Meta, const float *__restrict__ sw, void *__restrict__ out,
+    int M, int N, int K, int steps_per_wave) {
+    __shared__ int red[kSplit][MT][4][kWave];
+
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int n0 = blockIdx.x * 16;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int half = q >> 1, sub = q & 1;   // list half, 64-column step within the 128
+    const int steps64 = K / 64;
+    const int8_t *vrow = V + (int64_t)(n0 + r16) * (K / 2) + 16 * half;
+    const uint32_t *mrow = Meta + (int64_t)(n0 + r16) * (K / 32) + half;
+    const int8_t *xrow[MT];
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) xrow[mb] = X + (int64_t)min(mb * 16 + r16, M - 1) * K;
+
+    const int total_steps = (steps64 + 1) / 2;
+    const int s_begin = wave * steps_per_wave;
+    const int s_end = min(s_begin + steps_per_wave, total_steps);
+
+    v4i acc[MT];
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) acc[mb] = v4i{};
+    // Loads read in bounds (step and column clamped) and are masked afterwards:
+    // a zero weight operand cancels whatever activation bytes its partner
+    // lanes hold, so only the weight side needs the mask.
+    for (int s = s_begin; s < s_end; s += kUnroll) {
+        v4i a[kUnroll];
+        int idx[kUnroll];
+        v8i b[MT][kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int st = 2 * (s + u) + sub;
+            const int stc = min(st, steps64 - 1);
+            const bool ok = s + u < s_end && st < steps64;
+            const v4i av = *reinterpret_cast<const v4i *>(vrow + 32 * stc);
+            a[u] = ok ? av : v4i{};
+            idx[u] = (int)mrow[2 * stc];
+            const int kx = min(128 * (s + u) + 32 * q, K - 32);
+#pragma unroll
+            for (int mb = 0; mb < MT; ++mb) b[mb][u] = *reinterpret_cast<const v8i *>(xrow[mb] + kx);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int mb = 0; mb < MT; ++mb) acc[mb] = smfmac_16x16x128(a[u], b[mb][u], acc[mb], idx[u]);
+    }
+
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][mb][r][lane] = acc[mb][r];
+    __syncthreads();
+
+    // one output per thread: channel c (0..15) of row j of row block mb sits in
+    // lane j + 16 * (c / 4), element c % 4
+    for (int e = threadIdx.x; e < MT * 256; e += kSplit * kWave) {
+        const int mb = e >> 8, j = (e >> 4) & 15, c = e & 15;
+        const int m = mb * 16 + j;
+        if (m >= M) continue;
+        const int l = j + 16 * (c >> 2), r = c & 3;
+        int sum = 0;
+#pragma unroll
+        for (int w = 0; w < kSplit; ++w) sum += red[w][mb][r][l];
+        const int n = n0 + c;
+        if constexpr (OUT_I32)
+            static_cast<int32_t *>(out)[(int64_t)m * N + n] = sum;
+        else
+            static_cast<__bf16 *>(out)[(int64_t)m * N + n] = (__bf16)((float)sum * sx[m] * sw[n]);
+    }
+}
+
+template <int MT>
+hipError_t launch_decode_mt(const int8_t *xq, const float *xs, int M, const int8_t *values,
+                            const uint32_t *meta, const float *ws, int N, int K, void *out,
+                            bool out_i32, hipStream_t stream) {
+    const int total_steps = (K / 64 + 1) / 2;
+    const int steps_per_wave = (total_steps + kSplit - 1) / kSplit;
+    const dim3 grid((unsigned)(N / 16)), block(kSplit * kWave);
+    if (out_i32)
+        sparse24_decode_kernel<MT, true><<<grid, block, 0, stream>>>(xq, xs, values, meta, ws, out,
+                                                                      M, N, K, steps_per_wave);
+    else
+        sparse24_decode_kernel<MT, false><<<grid, block, 0, stream>>>(xq, xs, values, meta, ws, out,
+                                                                       M, N, K, steps_per_wave);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// LDS-tiled 2:4 GEMM for larger M: a workgroup of 4 wavefronts (2 x 2) computes
+// a 128-row x 256-channel tile with v_smfmac_i32_32x32x64_i8 (weights as the
+// sparse operand), K advancing 128 columns per stage through a ring of 3 LDS
+// stages filled with direct-to-LDS 16-byte loads, as the dense tiled kernel
+// does. The compressed weight is half the bytes of the dense one, so the tile
+// is wide in channels: per stage 16 KB of activations and 20 KB of weights.
+//
+// Stage layout (16-byte slots): activations, 128 rows x 8 slots, chunk c of
+// row r at slot c ^ (r % 8) ^ ((r / 8) % 2) (bank-conflict-free fragment
+// reads, as in the dense kernel); then weights, 256 rows x 5 slots: the row's
+// 64 value bytes of the stage (4 slots, in storage order) and its 4 index
+// words (one slot). The 80-byte row stride is an odd number of slots, so 8
+// consecutive rows reading the same slot hit distinct bank groups. Each
+// wavefront fills 4 + 5 whole 64-slot runs per stage; a lane's source is
+// whichever row piece its slot holds (values or meta array).
+//
+// Per 64-column step a lane reads, for each 32-row activation tile, the two
+// slots holding bytes [32 h, 32 h + 32) of the step (h = lane / 32), and for
+// each 32-channel weight tile the value slot of list half h and its index
+// word. Fragments of the next step are read while the current step's MFMAs run.
+constexpr int kTBM = 128, kTBN = 256, kTStages = 3;
+constexpr int kTThreads = 256;
+constexpr int kTXSlots = kTBM * 8, kTWSlots = kTBN * 5;
+constexpr int kTStage = kTXSlots + kTWSlots;     // 16-byte slots per stage
+constexpr int kTXLd = kTXSlots / (64 * 4);       // activation loads per wavefront per stage
+constexpr int kTWLd = kTWSlots / (64 * 4);       // weight loads per wavefront per stage
+constexpr int kTNld = kTXLd + kTWLd;
+constexpr int kTWM = 64, kTWN = 128;             // wavefront sub-tile
+constexpr int kTTM = kTWM / 32, kTTN = kTWN / 32;
+static_assert(kTXLd * 64 * 4 == kTXSlots && kTWLd * 64 * 4 == kTWSlots, "whole runs per wavefront");
+static_assert(kTBM * kTBN * 2 <= kTStages * kTStage * 16, "bf16 tile fits in the stage buffers");
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ v16i smfmac_32x32x64(v4i a, v8i b, v16i c, int idx) {
+    return __builtin_amdgcn_smfmac_i32_32x32x64_i8(a, b, c, idx, 0, 0);
+}
+
+struct TFrag {
+    v8i x[kTTM];
+    v4i w[kTTN];
+    int idx[kTTN];
+};
+
+template <bool OUT_I32>
+__global__ __launch_bounds__(kTThreads, 1) void sparse24_tiled_kernel(
+    const int8_t *__restrict__ X, const float *__restrict__ sx, const int8_t *__restrict__ V,
+    const uint32_t *__restrict__ Meta, const float *__restrict__ sw, void *__restrict__ out,
+    int M, int N, int K, int tiles_m, int tiles_n) {
+    __shared__ uint4 lds[kTStages * kTStage];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // tile order: XCD-contiguous, then groups of 4 tile rows
+    const int tiles = tiles_m * tiles_n;
+    const int t = xcd_contiguous(blockIdx.x, tiles);
+    constexpr int kGroup = 4;
+    const int per_group = kGroup * tiles_n;
+    const int first_m = (t / per_group) * kGroup;
+    const int gsize = min(tiles_m - first_m, kGroup);
+    const int m0 = (first_m + (t % per_group) % gsize) * kTBM;
+    const int n0 = ((t % per_group) / gsize) * kTBN;
+    const int nk = K / 128;
+
+    // per-lane sources of this wavefront's loads (stage 0; stage j adds j * inc)
+    const int8_t *xsrc[kTXLd];
+    {
+        const int row = 8 * wave + (lane >> 3);
+        const int kc = (lane & 7) ^ swz(row);
+#pragma unroll
+        for (int l = 0; l < kTXLd; ++l)
+            xsrc[l] = X + (int64_t)min(m0 + row + 32 * l, M - 1) * K + 16 * kc;
+    }
+    const int8_t *wsrc[kTWLd];
+    int winc[kTWLd];
+#pragma unroll
+    for (int l = 0; l < kTWLd; ++l) {
+        const int slot = 64 * (wave + 4 * l) + lane;
+        const int row = slot / 5, c = slot % 5;
+        const int64_t n = min(n0 + row, N - 1);
+        if (c < 4) {
+            wsrc[l] = V + n * (K / 2) + 16 * c;
+            winc[l] = 64;
+        } else {
+            wsrc[l] = reinterpret_cast<const int8_t *>(Meta + n * (K / 32));
+            winc[l] = 16;
+        }
+    }
+    auto load_stage = [&](int j, uint4 *buf) {
+#pragma unroll
+        for (int l = 0; l < kTXLd; ++l)
+            __builtin_amdgcn_global_load_lds((global_void *)(xsrc[l] + 128 * j),
+                                             (lds_void *)(buf + 64 * (wave + 4 * l)), 16, 0, 0);
+#pragma unroll
+        for (int l = 0; l < kTWLd; ++l)
+            __builtin_amdgcn_global_load_lds((global_void *)(wsrc[l] + winc[l] * j),
+                                             (lds_void *)(buf + kTXSlots + 64 * (wave + 4 * l)), 16,
+                                             0, 0);
+    };
+
+    const int frag_row = lane & 31, half = lane >> 5;
+    const int xrow0 = wm * kTWM + frag_row, wrow0 = wn * kTWN + frag_row;
+    const int fswz = swz(frag_row);
+    auto read_frags = [&](const uint4 *buf, int step, TFrag &f) {
+        const int c0 = (4 * step + 2 * half) ^ fswz, c1 = (4 * step + 2 * half + 1) ^ fswz;
+#pragma unroll
+        for (int i = 0; i < kTTM; ++i) {
+            const int r = xrow0 + 32 * i;   // r % 16 == frag_row % 16: same swizzle
+            const v4i lo = __builtin_bit_cast(v4i, buf[r * 8 + c0]);
+            const v4i hi = __builtin_bit_cast(v4i, buf[r * 8 + c1]);
+            f.x[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        const uint4 *wb = buf + kTXSlots;
+#pragma unroll
+        for (int j = 0; j < kTTN; ++j) {
+            const int r = wrow0 + 32 * j;
+            f.w[j] = __builtin_bit_cast(v4i, wb[r * 5 + 2 * step + half]);
+            f.idx[j] = reinterpret_cast<const int *>(wb + r * 5 + 4)[2 * step + half];
+        }
+    };
+
+    v16i acc[kTTM][kTTN];
+#pragma unroll
+    for (int i = 0; i < kTTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTTN; ++j) acc[i][j] = v16i{};
+    auto mma = [&](const TFrag &f) {
+#pragma unroll
+        for (int i = 0; i < kTTM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTTN; ++j) acc[i][j] = smfmac_32x32x64(f.w[j], f.x[i], acc[i][j], f.idx[j]);
+    };
+
+    auto stage_buf = [&](int j) { return lds + (j % kTStages) * kTStage; };
+    // prologue: stages 0 and 1 in flight, stage 0 landed everywhere
+    load_stage(0, stage_buf(0));
+    if (nk > 1) {
+        load_stage(1, stage_buf(1));
+        vm_barrier<kTNld>();
+    } else {
+        vm_barrier<0>();
+    }
+    TFrag f0, f1;
+    read_frags(stage_buf(0), 0, f0);
+    for (int s = 0; s < nk; ++s) {
+        const uint4 *cur = stage_buf(s);
+        const bool ahead = s + 2 < nk;   // uniform
+        if (ahead) load_stage(s + 2, stage_buf(s + 2));
+        read_frags(cur, 1, f1);
+        mma(f0);
+        // the next stage has landed from this wavefront (only the stage issued
+        // above may still be in flight) and its reads of this stage are done;
+        // after the barrier both hold for every wavefront
+        if (ahead)
+            vm_barrier<kTNld>();
+        else
+            vm_barrier<0>();
+        // (on the last stage this reads a stale buffer, in bounds and unused:
+        // unconditional, so the wait before the MFMAs below stays exact)
+        read_frags(stage_buf(s + 1), 0, f0);
+        mma(f1);
+    }
+    __syncthreads();  // all fragment reads done before the epilogue reuses LDS
+
+    // tile (i, j), element r of a lane: activation row i*32 + lane%32 of the
+    // wavefront's sub-tile, channel j*32 + 8*(r/4) + 4*half + r%4
+    const int mw0 = m0 + wm * kTWM, nw0 = n0 + wn * kTWN;
+    if constexpr (OUT_I32) {
+#pragma unroll
+        for (int i = 0; i < kTTM; ++i) {
+            const int m = mw0 + i * 32 + frag_row;
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < kTTN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = nw0 + j * 32 + 8 * g + 4 * half;
+                    if (n < N)
+                        __builtin_nontemporal_store(
+                            v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                acc[i][j][4 * g + 3]},
+                            reinterpret_cast<v4i *>(static_cast<int32_t *>(out) + (int64_t)m * N + n));
+                }
+        }
+    } else {
+        // stage the wavefront's 64 x 128 bf16 sub-tile in LDS (16-byte chunks of
+        // a row permuted by row % 8), then store whole 16-byte row pieces
+        constexpr int CH = kTWN / 8;
+        uint2 *st8 = reinterpret_cast<uint2 *>(lds) + wave * (kTWM * kTWN / 4);
+        float sxv[kTTM];
+#pragma unroll
+        for (int i = 0; i < kTTM; ++i) sxv[i] = sx[min(mw0 + i * 32 + frag_row, M - 1)];
+#pragma unroll
+        for (int j = 0; j < kTTN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = min(nw0 + j * 32 + 8 * g + 4 * half, N - 4);
+                const float4 w = *reinterpret_cast<const float4 *>(sw + n);
+#pragma unroll
+                for (int i = 0; i < kTTM; ++i) {
+                    const int ml = i * 32 + frag_row;
+                    const v16i &a = acc[i][j];
+                    const uint32_t lo = pack_bf16x2((float)a[4 * g] * sxv[i] * w.x,
+                                                    (float)a[4 * g + 1] * sxv[i] * w.y);
+                    const uint32_t hi = pack_bf16x2((float)a[4 * g + 2] * sxv[i] * w.z,
+                                                    (float)a[4 * g + 3] * sxv[i] * w.w);
+                    st8[(ml * CH + ((j * 4 + g) ^ (ml & 7))) * 2 + half] = make_uint2(lo, hi);
+                }
+            }
+        __syncthreads();
+        const uint4 *st16 = reinterpret_cast<const uint4 *>(st8);
+#pragma unroll
+        for (int it = 0; it < kTWM * CH / kWave; ++it) {
+            const int q = it * kWave + lane;
+            const int ml = q / CH, cc = q % CH;
+            const int m = mw0 + ml, n = nw0 + cc * 8;
+            const uint4 v = st16[ml * CH + (cc ^ (ml & 7))];
+            if (m < M && n < N) store16_nt(static_cast<__bf16 *>(out) + (int64_t)m * N + n, v);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_compress24(const int8_t *wq, int N, int K, int8_t *values, uint32_t *meta,
+                             hipStream_t stream) {
+    const int64_t chunks = (int64_t)N * (K / 32);
+    const dim3 grid((unsigned)((chunks + 255) / 256)), block(256);
+    compress24_kernel<<<grid, block, 0, stream>>>(wq, chunks, K, values, meta);
+    return hipGetLastError();
+}
+
+hipError_t launch_sparse24_gemm(const int8_t *xq, const float *xs, int M, const int8_t *values,
+                                const uint32_t *meta, const float *ws, int N, int K, void *out,
+                                bool out_i32, hipStream_t stream) {
+    switch ((M + 15) / 16) {
+        case 1: return launch_decode_mt<1>(xq, xs, M, values, meta, ws, N, K, out, out_i32, stream);
+        case 2: return launch_decode_mt<2>(xq, xs, M, values, meta, ws, N, K, out, out_i32, stream);
+        case 3: return launch_decode_mt<3>(xq, xs, M, values, meta, ws, N, K, out, out_i32, stream);
+        case 4: return launch_decode_mt<4>(xq, xs, M, values, meta, ws, N, K, out, out_i32, stream);
+        default: break;
+    }
+    const int tiles_m = (M + kTBM - 1) / kTBM, tiles_n = (N + kTBN - 1) / kTBN;
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kTThreads);
+    if (out_i32)
+        sparse24_tiled_kernel<true><<<grid, block, 0, stream>>>(xq, xs, values, meta, ws, out, M, N,
+                                                                K, tiles_m, tiles_n);
+    else
+        sparse24_tiled_kernel<false><<<grid, block, 0, stream>>>(xq, xs, values, meta, ws, out, M,
+                                                                 N, K, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace w8a8

@@ -32,8 +32,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_gemm_addmm",
-               "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_status_string",
-               "w8a8_last_hip_error"):
+               "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_compress24", "w8a8_sparse24_gemm",
+               "w8a8_status_string", "w8a8_last_hip_error"):
         assert fn in names
 
 
@@ -131,6 +131,37 @@ def test_fused_linear_validation(lib):
         assert f(*args(**{k: P + 2})) == ALIGN, k
     assert f(*args(bias=0, beta=0.0, M=0)) == OK        # no bias term, empty: no launch
     assert f(*args(M=0, x=0, out=0)) == OK
+
+
+def test_compress24_validation(lib):
+    c = lib.w8a8_compress24
+    args = lambda **kw: [kw.get("wq", P), kw.get("N", 32), kw.get("K", 128), kw.get("vals", P),
+                         kw.get("meta", P), None]
+    assert c(*args(N=-1)) == SHAPE
+    assert c(*args(K=0)) == SHAPE
+    assert c(*args(K=96)) == SHAPE                       # K % 64
+    for k in ("wq", "vals", "meta"):
+        assert c(*args(**{k: 0})) == NULL, k
+        assert c(*args(**{k: P + 4})) == ALIGN, k
+    assert c(*args(N=0, wq=0, vals=0, meta=0)) == OK
+
+
+def test_sparse24_gemm_validation(lib):
+    g = lib.w8a8_sparse24_gemm
+    args = lambda **kw: [kw.get("xq", P), kw.get("xs", P), kw.get("M", 16), kw.get("vals", P),
+                         kw.get("meta", P), kw.get("ws", P), kw.get("N", 64), kw.get("K", 128),
+                         kw.get("out", P), kw.get("od", 0), None]
+    assert g(*args(M=-1)) == SHAPE
+    assert g(*args(M=65, K=192)) == SHAPE                # M > 64 needs K % 128
+    assert g(*args(N=40)) == SHAPE
+    assert g(*args(K=96)) == SHAPE
+    assert g(*args(K=0)) == SHAPE
+    assert g(*args(K=133184)) == KOVF
+    assert g(*args(od=2)) == DTYPE
+    for k in ("xq", "xs", "vals", "meta", "ws", "out"):
+        assert g(*args(**{k: 0})) == NULL, k
+        assert g(*args(**{k: P + 8})) == ALIGN, k
+    assert g(*args(M=0, xq=0, xs=0, out=0)) == OK
 
 
 def test_bsr_validation(lib):

@@ -375,6 +375,102 @@ def test_fused_linear_limits(b):
                             beta=0.0)
 
 
+# --- 2:4 semi-structured weights ---------------------------------------------
+
+def _gpu_compress24(b, oracle, wq_dev, wq_ref, what):
+    """w8a8_compress24 bit-exact against the oracle's compression."""
+    values, meta = b.w8a8_compress24(wq_dev)
+    v_ref, m_ref = oracle.compress24(wq_ref)
+    torch.cuda.synchronize()
+    assert np.array_equal(values.cpu().numpy(), v_ref), f"{what}: values differ"
+    assert np.array_equal(meta.cpu().numpy().view(np.uint32), m_ref), f"{what}: meta differs"
+    return values, meta, v_ref, m_ref
+
+
+def test_compress24_dense_and_2to4(b, oracle):
+    """Pruning a dense int8 matrix (frequent equal magnitudes, int8 extremes) and storing a
+    2:4 weight exactly."""
+    log("compress24")
+    rng = np.random.default_rng(11)
+    w = rng.integers(-3, 4, size=(48, 320), dtype=np.int8)
+    w[0, :16] = -128
+    w[1, :16] = 127
+    _gpu_compress24(b, oracle, torch.from_numpy(w).to(DEV), w, "dense small-range")
+    inp = make_linear(4, 96, 512, seed=12, sparse24=True)
+    wq, sw, wq_ref, sw_ref = gpu_weights(b, oracle, inp.w)
+    values, meta, v_ref, m_ref = _gpu_compress24(b, oracle, wq, wq_ref, "2:4")
+    assert np.array_equal(oracle.decompress24(v_ref, m_ref), wq_ref)
+
+
+def _sparse24_case(b, oracle, M, N, K, seed, rows=None):
+    inp = make_linear(M, N, K, seed=seed, sparse24=True)
+    xq, sx, xq_ref, sx_ref = _check_quantize(b, oracle, inp.x_bits, f"M={M} N={N} K={K}")
+    wq, sw, wq_ref, sw_ref = gpu_weights(b, oracle, inp.w)
+    values, meta, v_ref, m_ref = _gpu_compress24(b, oracle, wq, wq_ref, f"N={N} K={K}")
+    w_dense = oracle.decompress24(v_ref, m_ref)
+    assert np.array_equal(w_dense, wq_ref)                  # the generator's weight is 2:4
+    rows = np.arange(M) if rows is None else rows
+    acc = b.w8a8_sparse24_gemm(xq, sx, values, meta, sw, out_dtype="i32").cpu().numpy()
+    out = bf16_bits(b.w8a8_sparse24_gemm(xq, sx, values, meta, sw))
+    acc_ref = oracle.gemm_i32(xq_ref[rows], w_dense)
+    bad = np.argwhere(acc[rows] != acc_ref)
+    assert bad.size == 0, f"int32 acc differs at {len(bad)} places, first {bad[:4].tolist()}"
+    return assert_bf16_close(out[rows], oracle.epilogue_bf16(acc_ref, sx_ref[rows], sw_ref),
+                             f"sparse24 M={M} N={N} K={K}")
+
+
+SPARSE24_SHAPES = [
+    # weight-streaming path (M <= 64; K a multiple of 64)
+    (1, 16, 64), (5, 48, 192), (3, 1040, 64), (16, 128, 4096), (17, 64, 320), (33, 32, 128),
+    (48, 160, 576), (64, 96, 512), (64, 256, 8192),
+    # tiled path (128 x 256 tiles; K a multiple of 128): ragged M and N, one and many tiles
+    (65, 256, 128), (129, 16, 128), (130, 272, 384), (300, 528, 256), (520, 1040, 1152),
+    (256, 512, 4096), (1100, 2064, 640),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SPARSE24_SHAPES)
+def test_sparse24_gemm_shapes(b, oracle, M, N, K):
+    log(f"sparse24 gemm M={M} N={N} K={K}")
+    _sparse24_case(b, oracle, M, N, K, seed=M + 5 * N + K)
+
+
+def test_sparse24_decode_workload_full_size(b, oracle):
+    name = "sparse24_decode"
+    cfg = CONFIGS[name]
+    log(f"sparse24 workload {name} {cfg}")
+    worst = _sparse24_case(b, oracle, cfg["M"], cfg["N"], cfg["K"], seed=0)
+    log(f"  {name}: max {worst} ulp")
+
+
+def test_sparse24_workload_full_size(b, oracle):
+    """The M=2048 2:4 layer in the benchmark's launch configuration, on sampled rows."""
+    name = "sparse24"
+    cfg = CONFIGS[name]
+    log(f"sparse24 workload {name} {cfg}")
+    inp = make_inputs(name)
+    xq, sx, xq_ref, sx_ref = _check_quantize(b, oracle, inp.x_bits, name)
+    wq, sw, wq_ref, sw_ref = gpu_weights(b, oracle, inp.w)
+    values, meta, v_ref, m_ref = _gpu_compress24(b, oracle, wq, wq_ref, name)
+    w_dense = oracle.decompress24(v_ref, m_ref)
+    rows = _sampled_rows(inp.M)
+    acc = b.w8a8_sparse24_gemm(xq, sx, values, meta, sw, out_dtype="i32").cpu().numpy()
+    out = bf16_bits(b.w8a8_sparse24_gemm(xq, sx, values, meta, sw))
+    acc_ref = oracle.gemm_i32(xq_ref[rows], w_dense)
+    assert np.array_equal(acc[rows], acc_ref)
+    worst = assert_bf16_close(out[rows], oracle.epilogue_bf16(acc_ref, sx_ref[rows], sw_ref), name)
+    log(f"  {name}: {len(rows)} rows x {inp.N} compared, max {worst} ulp")
+
+
+def test_sparse24_empty(b):
+    xq = torch.empty((0, 128), dtype=torch.int8, device=DEV)
+    xs = torch.empty((0,), dtype=torch.float32, device=DEV)
+    values = torch.zeros((32, 64), dtype=torch.int8, device=DEV)
+    meta = torch.zeros((32, 4), dtype=torch.int32, device=DEV)
+    ws = torch.ones((32,), dtype=torch.float32, device=DEV)
+    assert b.w8a8_sparse24_gemm(xq, xs, values, meta, ws).shape == (0, 32)
+
+
 # --- block-sparse GEMM ------------------------------------------------------
 
 def _bsr_case(b, oracle, M, N, K, zero_frac, seed, rows=None):
