@@ -183,18 +183,21 @@ w8a8_status w8a8_bsr_gemm(const int8_t *xq, const float *x_scale, int64_t M, int
  * sparse MFMA multiplies such a weight stored compressed, at half the weight
  * bytes and twice the dense MFMA rate.
  *
- * Compression of an int8 weight wq [N,K] (K a positive multiple of 64):
- *   values [N, K/2] int8 and meta [N, K/32] uint32 (all device, caller-owned).
+ * Compression of an int8 weight wq [N,K] (K a positive multiple of 128):
+ *   values [K/128, N, 64] int8 and meta [K/128, N, 4] uint32 (all device,
+ *   caller-owned).
  * Each group of 4 keeps the positions p0 < p1 of its two largest |w| (equal
  * magnitudes in position order), so a weight that already is 2:4 is stored
  * exactly; other weights are pruned to that pattern. Within each 64-column
  * step s the 16 groups are listed in the order 0,1,2,3, 8,9,10,11, 4,5,6,7,
- * 12,13,14,15 (list position c holds group g = 16 s + order[c]):
- *   values[n][32 s + 2 c + t] = wq[n][4 g + p_t]            (t = 0, 1)
- *   meta[n][2 s + c / 8] bits 4 (c % 8) .. +3 = p0 | p1 << 2
+ * 12,13,14,15 (list position c holds group g = 16 s + order[c]); with block
+ * B = s / 2 and e = s % 2:
+ *   values[B][n][32 e + 2 c + t] = wq[n][4 g + p_t]          (t = 0, 1)
+ *   meta[B][n][2 e + c / 8] bits 4 (c % 8) .. +3 = p0 | p1 << 2
  * (the lane layout of the sparse MFMA operand, so every fragment is one
- * contiguous load). w_scale stays the per-channel scale of wq.
- * Errors: NULL, SHAPE (N < 0, K <= 0, K % 64), ALIGN, HIP.
+ * contiguous load; block-major, so a tile of rows loads whole cache lines).
+ * w_scale stays the per-channel scale of wq.
+ * Errors: NULL, SHAPE (N < 0, K <= 0, K % 128), ALIGN, HIP.
  */
 w8a8_status w8a8_compress24(const int8_t *wq, int64_t N, int64_t K, int8_t *values,
                             uint32_t *meta, void *stream);
@@ -205,8 +208,7 @@ w8a8_status w8a8_compress24(const int8_t *wq, int64_t N, int64_t K, int8_t *valu
  *   acc = sum_k xq[m,k] * W[n,k], W the weight values/meta hold.
  * xq, x_scale, w_scale, out and out_dtype as for w8a8_gemm; values, meta from
  * w8a8_compress24. M >= 0 (M <= 64 takes a weight-streaming path, larger M an
- * LDS-tiled one), N a positive multiple of 16, K a positive multiple of 64,
- * and of 128 when M > 64.
+ * LDS-tiled one), N a positive multiple of 16, K a positive multiple of 128.
  * Errors: NULL, SHAPE, K_OVERFLOW, ALIGN, DTYPE, HIP.
  */
 w8a8_status w8a8_sparse24_gemm(const int8_t *xq, const float *x_scale, int64_t M,

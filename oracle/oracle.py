@@ -171,14 +171,14 @@ def bsr_gemm_i32(xq: np.ndarray, crow: np.ndarray, col: np.ndarray, values: np.n
 
 
 def compress24(w: np.ndarray):
-    """int8 [N,K] (K % 64 == 0) -> (values int8 [N,K/2], meta uint32 [N,K/32]): the two
-    largest magnitudes of each group of 4 along K, in the library's storage order."""
+    """int8 [N,K] (K % 128 == 0) -> (values int8 [K/128,N,64], meta uint32 [K/128,N,4]): the
+    two largest magnitudes of each group of 4 along K, in the library's storage order."""
     w = _c(w, np.int8)
     N, K = w.shape
-    if K % 64:
-        raise ValueError("K must be a multiple of 64")
-    values = np.empty((N, K // 2), np.int8)
-    meta = np.empty((N, K // 32), np.uint32)
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    values = np.empty((K // 128, N, 64), np.int8)
+    meta = np.empty((K // 128, N, 4), np.uint32)
     load_oracle().oracle_compress24(_ptr(w), N, K, _ptr(values), _ptr(meta))
     return values, meta
 
@@ -187,9 +187,9 @@ def decompress24(values: np.ndarray, meta: np.ndarray) -> np.ndarray:
     """The dense int8 [N,K] weight that compressed 2:4 arrays hold."""
     values = _c(values, np.int8)
     meta = _c(meta, np.uint32)
-    N, K2 = values.shape
-    K = 2 * K2
-    if K % 64 or meta.shape != (N, K // 32):
+    KB, N, width = values.shape
+    K = 128 * KB
+    if width != 64 or meta.shape != (KB, N, 4):
         raise ValueError("2:4 array shapes")
     w = np.empty((N, K), np.int8)
     if load_oracle().oracle_decompress24(_ptr(values), _ptr(meta), N, K, _ptr(w)) != 0:

@@ -217,19 +217,21 @@ int oracle_bsr_gemm_i32(const int8_t *xq, int64_t M, int64_t K, const int32_t *c
 }
 
 /*
- * 2:4 compression of an int8 weight w [N,K] (K % 64 == 0).
+ * 2:4 compression of an int8 weight w [N,K] (K % 128 == 0).
  *
  * Group g of row n is w[n][4g .. 4g+3]. Its kept positions p0 < p1 are the two
  * largest |w| of the group, equal magnitudes taken in position order (the
  * pages take weights that are already 2:4; with at most two nonzeros in a
  * group this keeps all of them, so such a weight is stored exactly).
  *
- * Storage, per row n and 64-column step s (groups 16s .. 16s+15): the groups
- * are listed in the order 0,1,2,3, 8,9,10,11, 4,5,6,7, 12,13,14,15 of the step,
- * list position c holding group 16s + order[c];
- *   values[n][32s + 2c + t] = w[n][4 (16s + order[c]) + p_t]      (t = 0, 1)
- *   meta[n][2s + c/8], bits 4 (c%8) .. 4 (c%8) + 3 = p0 | p1 << 2
- * values is int8 [N, K/2], meta uint32 [N, K/32].
+ * Storage. Within each 64-column step s (groups 16s .. 16s+15) the groups are
+ * listed in the order 0,1,2,3, 8,9,10,11, 4,5,6,7, 12,13,14,15 of the step,
+ * list position c holding group 16s + order[c]. The arrays are K-block-major:
+ * block B = s / 2 covers columns [128B, 128B+128), and every row's piece of a
+ * block is contiguous, rows in order:
+ *   values[B][n][32 (s % 2) + 2c + t] = w[n][4 (16s + order[c]) + p_t]  (t = 0, 1)
+ *   meta[B][n][2 (s % 2) + c/8], bits 4 (c%8) .. 4 (c%8) + 3 = p0 | p1 << 2
+ * values is int8 [K/128, N, 64], meta uint32 [K/128, N, 4].
  */
 static const int kGroupOrder24[16] = {0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15};
 
@@ -253,17 +255,19 @@ void oracle_compress24(const int8_t *w, int64_t N, int64_t K, int8_t *values, ui
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t s = 0; s < K / 64; ++s) {
+            int8_t *v = values + ((s / 2) * N + n) * 64 + 32 * (s % 2);
+            uint32_t *m = meta + ((s / 2) * N + n) * 4 + 2 * (s % 2);
             uint32_t words[2] = {0, 0};
             for (int c = 0; c < 16; ++c) {
                 const int8_t *grp = w + n * K + 4 * (16 * s + kGroupOrder24[c]);
                 int p0, p1;
                 kept_pair24(grp, &p0, &p1);
-                values[n * (K / 2) + 32 * s + 2 * c] = grp[p0];
-                values[n * (K / 2) + 32 * s + 2 * c + 1] = grp[p1];
+                v[2 * c] = grp[p0];
+                v[2 * c + 1] = grp[p1];
                 words[c / 8] |= (uint32_t)(p0 | (p1 << 2)) << (4 * (c % 8));
             }
-            meta[n * (K / 32) + 2 * s] = words[0];
-            meta[n * (K / 32) + 2 * s + 1] = words[1];
+            m[0] = words[0];
+            m[1] = words[1];
         }
     }
 }
@@ -277,13 +281,15 @@ int oracle_decompress24(const int8_t *values, const uint32_t *meta, int64_t N, i
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t k = 0; k < K; ++k) w[n * K + k] = 0;
         for (int64_t s = 0; s < K / 64; ++s) {
+            const int8_t *v = values + ((s / 2) * N + n) * 64 + 32 * (s % 2);
+            const uint32_t *m = meta + ((s / 2) * N + n) * 4 + 2 * (s % 2);
             for (int c = 0; c < 16; ++c) {
-                const uint32_t nib = (meta[n * (K / 32) + 2 * s + c / 8] >> (4 * (c % 8))) & 15u;
+                const uint32_t nib = (m[c / 8] >> (4 * (c % 8))) & 15u;
                 const int p0 = (int)(nib & 3u), p1 = (int)(nib >> 2);
                 if (!(p0 < p1)) bad = 1;
                 int8_t *grp = w + n * K + 4 * (16 * s + kGroupOrder24[c]);
-                grp[p0] = values[n * (K / 2) + 32 * s + 2 * c];
-                grp[p1] = values[n * (K / 2) + 32 * s + 2 * c + 1];
+                grp[p0] = v[2 * c];
+                grp[p1] = v[2 * c + 1];
             }
         }
     }

@@ -179,17 +179,17 @@ def w8a8_gemm_addmm(xq, x_scale, wq, w_scale, bias=None, alpha=1.0, beta=1.0, ou
 
 
 def w8a8_compress24(wq, values=None, meta=None, stream=None):
-    """int8 [N,K] weight -> (values int8 [N,K/2], meta int32 [N,K/32] holding the uint32
-    index words): the 2:4 storage of include/w8a8.h (two largest |w| per group of 4)."""
+    """int8 [N,K] weight -> (values int8 [K/128,N,64], meta int32 [K/128,N,4] holding the
+    uint32 index words): the 2:4 storage of include/w8a8.h (two largest |w| per group of 4)."""
     _check_tensor(wq, "wq", torch.int8, 2)
     N, K = wq.shape
     if values is None:
-        values = torch.empty((N, K // 2), dtype=torch.int8, device=wq.device)
+        values = torch.empty((K // 128, N, 64), dtype=torch.int8, device=wq.device)
     if meta is None:
-        meta = torch.empty((N, K // 32), dtype=torch.int32, device=wq.device)
-    _check_tensor(values, "values", torch.int8, 2)
-    _check_tensor(meta, "meta", torch.int32, 2)
-    if tuple(values.shape) != (N, K // 2) or tuple(meta.shape) != (N, K // 32):
+        meta = torch.empty((K // 128, N, 4), dtype=torch.int32, device=wq.device)
+    _check_tensor(values, "values", torch.int8, 3)
+    _check_tensor(meta, "meta", torch.int32, 3)
+    if tuple(values.shape) != (K // 128, N, 64) or tuple(meta.shape) != (K // 128, N, 4):
         raise ValueError("2:4 array shapes")
     _call("w8a8_compress24", wq.data_ptr(), N, K, values.data_ptr(), meta.data_ptr(),
           _stream_handle(stream))
@@ -198,16 +198,16 @@ def w8a8_compress24(wq, values=None, meta=None, stream=None):
 
 def w8a8_sparse24_gemm(xq, x_scale, values, meta, w_scale, out=None, out_dtype="bf16",
                        stream=None):
-    """W8A8 GEMM on a compressed 2:4 weight (values [N,K/2] int8, meta [N,K/32] int32)."""
+    """W8A8 GEMM on a compressed 2:4 weight (values [K/128,N,64] int8, meta [K/128,N,4] int32)."""
     od = _out_dtype(out_dtype)
     _check_tensor(xq, "xq", torch.int8, 2)
     _check_tensor(x_scale, "x_scale", torch.float32, 1)
-    _check_tensor(values, "values", torch.int8, 2)
-    _check_tensor(meta, "meta", torch.int32, 2)
+    _check_tensor(values, "values", torch.int8, 3)
+    _check_tensor(meta, "meta", torch.int32, 3)
     _check_tensor(w_scale, "w_scale", torch.float32, 1)
     M, K = xq.shape
     N = w_scale.shape[0]
-    if (tuple(values.shape) != (N, K // 2) or tuple(meta.shape) != (N, K // 32)
+    if (tuple(values.shape) != (K // 128, N, 64) or tuple(meta.shape) != (K // 128, N, 4)
             or tuple(x_scale.shape) != (M,)):
         raise ValueError("operand shapes")
     out = _out(out, M, N, od, xq.device)

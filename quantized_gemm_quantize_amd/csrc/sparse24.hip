@@ -17,7 +17,11 @@
 // [32h, 32h+32) of the step in the other operand; v_smfmac_i32_16x16x128_i8
 // takes, in lane quarter q, list half q / 2 of 64-column step q % 2 against
 // activation bytes [32q, 32q+32) of its 128 columns. So every operand fragment
-// is one contiguous 16-byte load plus one 32-bit index.
+// is one contiguous 16-byte load plus one 32-bit index. The arrays are
+// K-block-major ([K/128][N][64] values, [K/128][N][4] index words): the
+// pieces of one 128-column block for consecutive rows are contiguous, so a
+// tile of rows loads whole cache lines (per row and block there are only 64
+// value bytes and 16 index bytes).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -52,19 +56,20 @@ __device__ __forceinline__ void keep_two(uint32_t grp, uint32_t &nib, uint32_t &
     vals = ((uint32_t)w[p0] & 0xFFu) | (((uint32_t)w[p1] & 0xFFu) << 8);
 }
 
-// One thread per (row, 64-column step, list half): reads the 32 weights of its
-// 8 groups (columns [16h, 16h+16) and [32+16h, 32+16h+16) of the step), writes
-// 16 value bytes and one index word.
+// One thread per (128-column block, row, 64-column step, list half), in
+// storage order: reads the 32 weights of its 8 groups (columns [16h, 16h+16)
+// and [32+16h, 32+16h+16) of the step), writes 16 value bytes and one index
+// word.
 __global__ __launch_bounds__(256) void compress24_kernel(const int8_t *__restrict__ w,
-                                                          int64_t chunks, int K,
+                                                          int64_t chunks, int N, int K,
                                                           int8_t *__restrict__ values,
                                                           uint32_t *__restrict__ meta) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= chunks) return;
-    const int per_row = K / 32;  // two chunks per 64-column step
-    const int64_t n = t / per_row;
-    const int c = (int)(t % per_row), s = c >> 1, h = c & 1;
-    const int8_t *row = w + n * K + 64 * s + 16 * h;
+    const int h = (int)(t & 1), sub = (int)((t >> 1) & 1);
+    const int64_t bn = t >> 2;                 // block * N + row
+    const int64_t n = bn % N, blk = bn / N;
+    const int8_t *row = w + n * K + 128 * blk + 64 * sub + 16 * h;
     const uint4 lo = *reinterpret_cast<const uint4 *>(row);        // groups 4h .. 4h+3
     const uint4 hi = *reinterpret_cast<const uint4 *>(row + 32);   // groups 8+4h .. 8+4h+3
     const uint32_t grp[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -76,8 +81,8 @@ __global__ __launch_bounds__(256) void compress24_kernel(const int8_t *__restric
         word |= nib << (4 * i);
         v[i >> 1] |= vals << (16 * (i & 1));
     }
-    *reinterpret_cast<uint4 *>(values + n * (K / 2) + 32 * s + 16 * h) = make_uint4(v[0], v[1], v[2], v[3]);
-    meta[n * per_row + c] = word;
+    reinterpret_cast<uint4 *>(values)[t] = make_uint4(v[0], v[1], v[2], v[3]);
+    meta[t] = word;
 }
 
 // Weight-streaming 2:4 GEMM for M <= 64: the shape of the dense M-small kernel
@@ -99,39 +104,40 @@ __global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_kernel(
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int n0 = blockIdx.x * 16;
     const int r16 = lane & 15, q = lane >> 4;
-    const int half = q >> 1, sub = q & 1;   // list half, 64-column step within the 128
-    const int steps64 = K / 64;
-    const int8_t *vrow = V + (int64_t)(n0 + r16) * (K / 2) + 16 * half;
-    const uint32_t *mrow = Meta + (int64_t)(n0 + r16) * (K / 32) + half;
+    // lane quarter q = 2 * half + sub takes list half `half` of 64-column step
+    // `sub` of each 128-column block: 16 value bytes at 32 * sub + 16 * half
+    // of the row's 64, index word 2 * sub + half of its 4
+    const int half = q >> 1, sub = q & 1;
+    const int nblk = K / 128;
+    const int8_t *vrow = V + (int64_t)(n0 + r16) * 64 + 32 * sub + 16 * half;
+    const uint32_t *mrow = Meta + (int64_t)(n0 + r16) * 4 + 2 * sub + half;
+    const int64_t vstride = (int64_t)N * 64, mstride = (int64_t)N * 4;   // per block
     const int8_t *xrow[MT];
 #pragma unroll
     for (int mb = 0; mb < MT; ++mb) xrow[mb] = X + (int64_t)min(mb * 16 + r16, M - 1) * K;
 
-    const int total_steps = (steps64 + 1) / 2;
     const int s_begin = wave * steps_per_wave;
-    const int s_end = min(s_begin + steps_per_wave, total_steps);
+    const int s_end = min(s_begin + steps_per_wave, nblk);
 
     v4i acc[MT];
 #pragma unroll
     for (int mb = 0; mb < MT; ++mb) acc[mb] = v4i{};
-    // Loads read in bounds (step and column clamped) and are masked afterwards:
-    // a zero weight operand cancels whatever activation bytes its partner
-    // lanes hold, so only the weight side needs the mask.
+    // Loads past the wavefront's blocks read block nblk - 1 (in bounds) and
+    // are masked: a zero weight operand cancels whatever activation bytes
+    // its partner lanes hold, so only the weight side needs the mask.
     for (int s = s_begin; s < s_end; s += kUnroll) {
         v4i a[kUnroll];
         int idx[kUnroll];
         v8i b[MT][kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int st = 2 * (s + u) + sub;
-            const int stc = min(st, steps64 - 1);
-            const bool ok = s + u < s_end && st < steps64;
-            const v4i av = *reinterpret_cast<const v4i *>(vrow + 32 * stc);
-            a[u] = ok ? av : v4i{};
-            idx[u] = (int)mrow[2 * stc];
-            const int kx = min(128 * (s + u) + 32 * q, K - 32);
+            const int blk = min(s + u, nblk - 1);
+            const v4i av = *reinterpret_cast<const v4i *>(vrow + blk * vstride);
+            a[u] = s + u < s_end ? av : v4i{};
+            idx[u] = (int)mrow[blk * mstride];
 #pragma unroll
-            for (int mb = 0; mb < MT; ++mb) b[mb][u] = *reinterpret_cast<const v8i *>(xrow[mb] + kx);
+            for (int mb = 0; mb < MT; ++mb)
+                b[mb][u] = *reinterpret_cast<const v8i *>(xrow[mb] + 128 * blk + 32 * q);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
@@ -167,8 +173,7 @@ template <int MT>
 hipError_t launch_decode_mt(const int8_t *xq, const float *xs, int M, const int8_t *values,
                             const uint32_t *meta, const float *ws, int N, int K, void *out,
                             bool out_i32, hipStream_t stream) {
-    const int total_steps = (K / 64 + 1) / 2;
-    const int steps_per_wave = (total_steps + kSplit - 1) / kSplit;
+    const int steps_per_wave = (K / 128 + kSplit - 1) / kSplit;   // 128-column blocks
     const dim3 grid((unsigned)(N / 16)), block(kSplit * kWave);
     if (out_i32)
         sparse24_decode_kernel<MT, true><<<grid, block, 0, stream>>>(xq, xs, values, meta, ws, out,
@@ -182,40 +187,46 @@ hipError_t launch_decode_mt(const int8_t *xq, const float *xs, int M, const int8
 // ---------------------------------------------------------------------------
 // LDS-tiled 2:4 GEMM for larger M: a workgroup of 4 wavefronts (2 x 2) computes
 // a 128-row x 256-channel tile with v_smfmac_i32_32x32x64_i8 (weights as the
-// sparse operand), K advancing 128 columns per stage through a ring of 3 LDS
+// sparse operand), K advancing 128 columns per stage through a ring of 4 LDS
 // stages filled with direct-to-LDS 16-byte loads, as the dense tiled kernel
 // does. The compressed weight is half the bytes of the dense one, so the tile
-// is wide in channels: per stage 16 KB of activations and 20 KB of weights.
+// is wide in channels: per stage 16 KB of activations and 20 KB of weights,
+// and the 144 KB ring keeps three stages in flight (the loop is bound by how
+// many operand bytes are on their way from L2, not by the MFMAs).
 //
 // Stage layout (16-byte slots): activations, 128 rows x 8 slots, chunk c of
 // row r at slot c ^ (r % 8) ^ ((r / 8) % 2) (bank-conflict-free fragment
-// reads, as in the dense kernel); then weights, 256 rows x 5 slots: the row's
-// 64 value bytes of the stage (4 slots, in storage order) and its 4 index
-// words (one slot). The 80-byte row stride is an odd number of slots, so 8
-// consecutive rows reading the same slot hit distinct bank groups. Each
-// wavefront fills 4 + 5 whole 64-slot runs per stage; a lane's source is
-// whichever row piece its slot holds (values or meta array).
+// reads, as in the dense kernel); the weights' 64 value bytes per row, 256
+// rows x 4 slots, chunk c of row r at slot c ^ ((r / 2) % 4) (the same: 8
+// consecutive rows reading one chunk hit 8 distinct 16-byte bank groups); the
+// weights' 4 index words per row, 256 slots. In the K-block-major storage a
+// block's pieces of the tile's 256 weight rows are contiguous (16 KB of
+// values, 4 KB of index words), so every 64-lane load moves whole cache
+// lines. Each wavefront issues 4 + 4 + 1 loads per stage.
 //
 // Per 64-column step a lane reads, for each 32-row activation tile, the two
 // slots holding bytes [32 h, 32 h + 32) of the step (h = lane / 32), and for
 // each 32-channel weight tile the value slot of list half h and its index
 // word. Fragments of the next step are read while the current step's MFMAs run.
-constexpr int kTBM = 128, kTBN = 256, kTStages = 3;
+constexpr int kTBM = 128, kTBN = 256, kTStages = 4;
 constexpr int kTThreads = 256;
-constexpr int kTXSlots = kTBM * 8, kTWSlots = kTBN * 5;
-constexpr int kTStage = kTXSlots + kTWSlots;     // 16-byte slots per stage
-constexpr int kTXLd = kTXSlots / (64 * 4);       // activation loads per wavefront per stage
-constexpr int kTWLd = kTWSlots / (64 * 4);       // weight loads per wavefront per stage
-constexpr int kTNld = kTXLd + kTWLd;
-constexpr int kTWM = 64, kTWN = 128;             // wavefront sub-tile
+constexpr int kTXSlots = kTBM * 8, kTVSlots = kTBN * 4, kTMSlots = kTBN;
+constexpr int kTStage = kTXSlots + kTVSlots + kTMSlots;   // 16-byte slots per stage
+constexpr int kTXLd = kTXSlots / (64 * 4);                // loads per wavefront per stage
+constexpr int kTVLd = kTVSlots / (64 * 4);
+constexpr int kTMLd = kTMSlots / (64 * 4);
+constexpr int kTNld = kTXLd + kTVLd + kTMLd;
+constexpr int kTWM = 64, kTWN = 128;                      // wavefront sub-tile
 constexpr int kTTM = kTWM / 32, kTTN = kTWN / 32;
-static_assert(kTXLd * 64 * 4 == kTXSlots && kTWLd * 64 * 4 == kTWSlots, "whole runs per wavefront");
+static_assert(kTXLd * 256 == kTXSlots && kTVLd * 256 == kTVSlots && kTMLd * 256 == kTMSlots,
+              "whole runs per wavefront");
 static_assert(kTBM * kTBN * 2 <= kTStages * kTStage * 16, "bf16 tile fits in the stage buffers");
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 3; }
 
 __device__ __forceinline__ v16i smfmac_32x32x64(v4i a, v8i b, v16i c, int idx) {
     return __builtin_amdgcn_smfmac_i32_32x32x64_i8(a, b, c, idx, 0, 0);
@@ -256,31 +267,29 @@ __global__ __launch_bounds__(kTThreads, 1) void sparse24_tiled_kernel(
         for (int l = 0; l < kTXLd; ++l)
             xsrc[l] = X + (int64_t)min(m0 + row + 32 * l, M - 1) * K + 16 * kc;
     }
-    const int8_t *wsrc[kTWLd];
-    int winc[kTWLd];
+    const int8_t *vsrc[kTVLd];
 #pragma unroll
-    for (int l = 0; l < kTWLd; ++l) {
+    for (int l = 0; l < kTVLd; ++l) {
         const int slot = 64 * (wave + 4 * l) + lane;
-        const int row = slot / 5, c = slot % 5;
-        const int64_t n = min(n0 + row, N - 1);
-        if (c < 4) {
-            wsrc[l] = V + n * (K / 2) + 16 * c;
-            winc[l] = 64;
-        } else {
-            wsrc[l] = reinterpret_cast<const int8_t *>(Meta + n * (K / 32));
-            winc[l] = 16;
-        }
+        const int row = slot >> 2, c = (slot & 3) ^ vswz(row);
+        vsrc[l] = V + (int64_t)min(n0 + row, N - 1) * 64 + 16 * c;
     }
+    const uint32_t *msrc = Meta + (int64_t)min(n0 + 64 * wave + lane, N - 1) * 4;
+    static_assert(kTMLd == 1, "one index-word load per wavefront");
+    const int64_t vstride = (int64_t)N * 64, mstride = (int64_t)N * 4;   // per block
     auto load_stage = [&](int j, uint4 *buf) {
 #pragma unroll
         for (int l = 0; l < kTXLd; ++l)
             __builtin_amdgcn_global_load_lds((global_void *)(xsrc[l] + 128 * j),
                                              (lds_void *)(buf + 64 * (wave + 4 * l)), 16, 0, 0);
 #pragma unroll
-        for (int l = 0; l < kTWLd; ++l)
-            __builtin_amdgcn_global_load_lds((global_void *)(wsrc[l] + winc[l] * j),
+        for (int l = 0; l < kTVLd; ++l)
+            __builtin_amdgcn_global_load_lds((global_void *)(vsrc[l] + j * vstride),
                                              (lds_void *)(buf + kTXSlots + 64 * (wave + 4 * l)), 16,
                                              0, 0);
+        __builtin_amdgcn_global_load_lds((global_void *)(msrc + j * mstride),
+                                         (lds_void *)(buf + kTXSlots + kTVSlots + 64 * wave), 16, 0,
+                                         0);
     };
 
     const int frag_row = lane & 31, half = lane >> 5;
@@ -295,12 +304,13 @@ __global__ __launch_bounds__(kTThreads, 1) void sparse24_tiled_kernel(
             const v4i hi = __builtin_bit_cast(v4i, buf[r * 8 + c1]);
             f.x[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
-        const uint4 *wb = buf + kTXSlots;
+        const uint4 *vb = buf + kTXSlots, *mb = buf + kTXSlots + kTVSlots;
+        const int vc = (2 * step + half) ^ vswz(frag_row);   // (r / 2) % 4 == (frag_row / 2) % 4
 #pragma unroll
         for (int j = 0; j < kTTN; ++j) {
             const int r = wrow0 + 32 * j;
-            f.w[j] = __builtin_bit_cast(v4i, wb[r * 5 + 2 * step + half]);
-            f.idx[j] = reinterpret_cast<const int *>(wb + r * 5 + 4)[2 * step + half];
+            f.w[j] = __builtin_bit_cast(v4i, vb[r * 4 + vc]);
+            f.idx[j] = reinterpret_cast<const int *>(mb + r)[2 * step + half];
         }
     };
 
@@ -309,41 +319,53 @@ __global__ __launch_bounds__(kTThreads, 1) void sparse24_tiled_kernel(
     for (int i = 0; i < kTTM; ++i)
 #pragma unroll
         for (int j = 0; j < kTTN; ++j) acc[i][j] = v16i{};
-    auto mma = [&](const TFrag &f) {
+    // One step's MFMAs on fragments f, with `reads` (the next step's fragment
+    // reads) issued right after the first one: the wait before that first MFMA
+    // (the compiler waits for all LDS reads) then finds reads issued a whole
+    // step earlier, and the new reads land while the other MFMAs run.
+    auto mma_then_read = [&](const TFrag &f, auto &&reads) {
+        acc[0][0] = smfmac_32x32x64(f.w[0], f.x[0], acc[0][0], f.idx[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        reads();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < kTTM; ++i)
-#pragma unroll
-            for (int j = 0; j < kTTN; ++j) acc[i][j] = smfmac_32x32x64(f.w[j], f.x[i], acc[i][j], f.idx[j]);
+        for (int q = 1; q < kTTM * kTTN; ++q) {
+            const int i = q / kTTN, j = q % kTTN;
+            acc[i][j] = smfmac_32x32x64(f.w[j], f.x[i], acc[i][j], f.idx[j]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     auto stage_buf = [&](int j) { return lds + (j % kTStages) * kTStage; };
-    // prologue: stages 0 and 1 in flight, stage 0 landed everywhere
-    load_stage(0, stage_buf(0));
-    if (nk > 1) {
-        load_stage(1, stage_buf(1));
-        vm_barrier<kTNld>();
-    } else {
-        vm_barrier<0>();
-    }
+    // barrier after which stage j has landed for every wavefront, when `later`
+    // stages were issued after it (their loads may stay in flight)
+    auto stage_landed = [&](int later) {
+        static_assert(kTStages <= 4, "waits below cover up to 2 later stages");
+        if (later >= 2)
+            vm_barrier<2 * kTNld>();
+        else if (later == 1)
+            vm_barrier<kTNld>();
+        else
+            vm_barrier<0>();
+    };
+    // prologue: stages 0 .. kTStages-2 in flight, stage 0 landed everywhere
+    const int pre = min(kTStages - 1, nk);
+    for (int j = 0; j < pre; ++j) load_stage(j, stage_buf(j));
+    stage_landed(pre - 1);
     TFrag f0, f1;
     read_frags(stage_buf(0), 0, f0);
     for (int s = 0; s < nk; ++s) {
         const uint4 *cur = stage_buf(s);
-        const bool ahead = s + 2 < nk;   // uniform
-        if (ahead) load_stage(s + 2, stage_buf(s + 2));
-        read_frags(cur, 1, f1);
-        mma(f0);
-        // the next stage has landed from this wavefront (only the stage issued
-        // above may still be in flight) and its reads of this stage are done;
-        // after the barrier both hold for every wavefront
-        if (ahead)
-            vm_barrier<kTNld>();
-        else
-            vm_barrier<0>();
-        // (on the last stage this reads a stale buffer, in bounds and unused:
-        // unconditional, so the wait before the MFMAs below stays exact)
-        read_frags(stage_buf(s + 1), 0, f0);
-        mma(f1);
+        // the buffer refilled here was last read in stage s - 1, before its barrier
+        if (s + kTStages - 1 < nk) load_stage(s + kTStages - 1, stage_buf(s + kTStages - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        mma_then_read(f0, [&] { read_frags(cur, 1, f1); });
+        // the next stage has landed from this wavefront (only stages issued
+        // after it may still be in flight) and its reads of this stage are
+        // done; after the barrier both hold for every wavefront. (On the last
+        // stage the reads below fetch a stale buffer, in bounds and unused.)
+        stage_landed(min(kTStages - 2, nk - 2 - s));
+        mma_then_read(f1, [&] { read_frags(stage_buf(s + 1), 0, f0); });
     }
     __syncthreads();  // all fragment reads done before the epilogue reuses LDS
 
@@ -409,9 +431,9 @@ __global__ __launch_bounds__(kTThreads, 1) void sparse24_tiled_kernel(
 
 hipError_t launch_compress24(const int8_t *wq, int N, int K, int8_t *values, uint32_t *meta,
                              hipStream_t stream) {
-    const int64_t chunks = (int64_t)N * (K / 32);
+    const int64_t chunks = (int64_t)N * (K / 32);   // 16-byte value pieces = index words
     const dim3 grid((unsigned)((chunks + 255) / 256)), block(256);
-    compress24_kernel<<<grid, block, 0, stream>>>(wq, chunks, K, values, meta);
+    compress24_kernel<<<grid, block, 0, stream>>>(wq, chunks, N, K, values, meta);
     return hipGetLastError();
 }
 

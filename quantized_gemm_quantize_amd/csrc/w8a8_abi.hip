@@ -163,7 +163,7 @@ w8a8_status w8a8_bsr_gemm(const int8_t *xq, const float *x_scale, int64_t M, int
 
 w8a8_status w8a8_compress24(const int8_t *wq, int64_t N, int64_t K, int8_t *values,
                             uint32_t *meta, void *stream) {
-    if (N < 0 || K <= 0 || K % 64 != 0 || N > INT_MAX / 2 || K > INT_MAX / 2) return W8A8_ERR_SHAPE;
+    if (N < 0 || K <= 0 || K % 128 != 0 || N > INT_MAX / 2 || K > INT_MAX / 2) return W8A8_ERR_SHAPE;
     if (N == 0) return W8A8_OK;
     if (N * (K / 32) > (int64_t)UINT_MAX * 256 / 2) return W8A8_ERR_SHAPE;  // grid.x
     if (!wq || !values || !meta) return W8A8_ERR_NULL;
@@ -176,10 +176,9 @@ w8a8_status w8a8_sparse24_gemm(const int8_t *xq, const float *x_scale, int64_t M
                                const int8_t *values, const uint32_t *meta, const float *w_scale,
                                int64_t N, int64_t K, void *out, w8a8_out_dtype out_dtype,
                                void *stream) {
-    if (M < 0 || N <= 0 || N % 16 != 0 || K % 64 != 0 || too_big(M, N)) return W8A8_ERR_SHAPE;
+    if (M < 0 || N <= 0 || N % 16 != 0 || K % 128 != 0 || too_big(M, N)) return W8A8_ERR_SHAPE;
     if (w8a8_status s = check_k(K)) return s;
     if (out_dtype != W8A8_OUT_BF16 && out_dtype != W8A8_OUT_I32) return W8A8_ERR_DTYPE;
-    if (M > 64 && K % 128 != 0) return W8A8_ERR_SHAPE;             // the tiled kernel's stage
     if ((M + 127) / 128 > INT_MAX / ((N + 255) / 256)) return W8A8_ERR_SHAPE;  // grid.x
     if (M == 0) return W8A8_OK;
     if (!xq || !x_scale || !values || !meta || !w_scale || !out) return W8A8_ERR_NULL;

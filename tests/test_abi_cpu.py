@@ -139,7 +139,7 @@ def test_compress24_validation(lib):
                          kw.get("meta", P), None]
     assert c(*args(N=-1)) == SHAPE
     assert c(*args(K=0)) == SHAPE
-    assert c(*args(K=96)) == SHAPE                       # K % 64
+    assert c(*args(K=192)) == SHAPE                      # K % 128
     for k in ("wq", "vals", "meta"):
         assert c(*args(**{k: 0})) == NULL, k
         assert c(*args(**{k: P + 4})) == ALIGN, k
@@ -152,11 +152,11 @@ def test_sparse24_gemm_validation(lib):
                          kw.get("meta", P), kw.get("ws", P), kw.get("N", 64), kw.get("K", 128),
                          kw.get("out", P), kw.get("od", 0), None]
     assert g(*args(M=-1)) == SHAPE
-    assert g(*args(M=65, K=192)) == SHAPE                # M > 64 needs K % 128
+    assert g(*args(K=192)) == SHAPE                      # K % 128
+    assert g(*args(M=300, K=192)) == SHAPE
     assert g(*args(N=40)) == SHAPE
-    assert g(*args(K=96)) == SHAPE
     assert g(*args(K=0)) == SHAPE
-    assert g(*args(K=133184)) == KOVF
+    assert g(*args(K=133248)) == KOVF
     assert g(*args(od=2)) == DTYPE
     for k in ("xq", "xs", "vals", "meta", "ws", "out"):
         assert g(*args(**{k: 0})) == NULL, k

@@ -392,7 +392,7 @@ def test_compress24_dense_and_2to4(b, oracle):
     2:4 weight exactly."""
     log("compress24")
     rng = np.random.default_rng(11)
-    w = rng.integers(-3, 4, size=(48, 320), dtype=np.int8)
+    w = rng.integers(-3, 4, size=(48, 384), dtype=np.int8)
     w[0, :16] = -128
     w[1, :16] = 127
     _gpu_compress24(b, oracle, torch.from_numpy(w).to(DEV), w, "dense small-range")
@@ -420,10 +420,10 @@ def _sparse24_case(b, oracle, M, N, K, seed, rows=None):
 
 
 SPARSE24_SHAPES = [
-    # weight-streaming path (M <= 64; K a multiple of 64)
-    (1, 16, 64), (5, 48, 192), (3, 1040, 64), (16, 128, 4096), (17, 64, 320), (33, 32, 128),
-    (48, 160, 576), (64, 96, 512), (64, 256, 8192),
-    # tiled path (128 x 256 tiles; K a multiple of 128): ragged M and N, one and many tiles
+    # weight-streaming path (M <= 64)
+    (1, 16, 128), (5, 48, 384), (3, 1040, 128), (16, 128, 4096), (17, 64, 640), (33, 32, 128),
+    (48, 160, 1152), (64, 96, 512), (64, 256, 8192),
+    # tiled path (128 x 256 tiles): ragged M and N, one and many tiles and stages
     (65, 256, 128), (129, 16, 128), (130, 272, 384), (300, 528, 256), (520, 1040, 1152),
     (256, 512, 4096), (1100, 2064, 640),
 ]
@@ -465,8 +465,8 @@ def test_sparse24_workload_full_size(b, oracle):
 def test_sparse24_empty(b):
     xq = torch.empty((0, 128), dtype=torch.int8, device=DEV)
     xs = torch.empty((0,), dtype=torch.float32, device=DEV)
-    values = torch.zeros((32, 64), dtype=torch.int8, device=DEV)
-    meta = torch.zeros((32, 4), dtype=torch.int32, device=DEV)
+    values = torch.zeros((1, 32, 64), dtype=torch.int8, device=DEV)
+    meta = torch.zeros((1, 32, 4), dtype=torch.int32, device=DEV)
     ws = torch.ones((32,), dtype=torch.float32, device=DEV)
     assert b.w8a8_sparse24_gemm(xq, xs, values, meta, ws).shape == (0, 32)
 

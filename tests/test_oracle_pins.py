@@ -346,18 +346,20 @@ def test_prefill_outlier_channels():
 
 # --- 2:4 semi-structured weights --------------------------------------------
 
-def test_compress24_hand_worked_row(oracle):
-    """The storage of one 2:4 row, worked by hand from its definition."""
+def test_compress24_hand_worked_rows(oracle):
+    """The storage of two 2:4 rows (one 128-column block), worked by hand from its definition."""
     g = _load("sparse24_row.json")
-    row = np.zeros(64, np.int8)
-    for grp in range(16):
+    rows = np.zeros((2, 128), np.int8)
+    for grp in range(32):
         p0, p1 = g["pairs"][grp % 6]
-        row[4 * grp + p0] = grp + 1
-        row[4 * grp + p1] = -(grp + 1)
-    values, meta = oracle.compress24(row[None, :])
+        rows[0, 4 * grp + p0] = grp + 1
+        rows[0, 4 * grp + p1] = -(grp + 1)
+    rows[1] = -rows[0]
+    values, meta = oracle.compress24(rows)
+    assert values.shape == (1, 2, 64) and meta.shape == (1, 2, 4)
     assert values[0].tolist() == g["values"]
-    assert [int(m) for m in meta[0]] == [int(h, 16) for h in g["meta"]]
-    assert np.array_equal(oracle.decompress24(values, meta)[0], row)
+    assert [[int(m) for m in r] for r in meta[0]] == [[int(h, 16) for h in r] for r in g["meta"]]
+    assert np.array_equal(oracle.decompress24(values, meta), rows)
 
 
 def _brute_force_prune24(w: np.ndarray) -> np.ndarray:
@@ -377,7 +379,7 @@ def test_compress24_keeps_the_two_largest_magnitudes(oracle):
     """On a dense int8 matrix the stored weight is the brute-force top-2 selection, ties
     included (small value range so that equal magnitudes are frequent)."""
     rng = np.random.default_rng(24)
-    w = rng.integers(-3, 4, size=(9, 192), dtype=np.int8)
+    w = rng.integers(-3, 4, size=(9, 384), dtype=np.int8)
     w[0, :8] = -128                                   # int8 extremes
     w[1, :8] = 127
     values, meta = oracle.compress24(w)
@@ -397,8 +399,8 @@ def test_compress24_is_lossless_on_2to4_weights(oracle):
 
 
 def test_decompress24_rejects_bad_positions(oracle):
-    values = np.zeros((1, 32), np.int8)
-    meta = np.array([[0x44444444, 0x44444441]], np.uint32)   # last nibble: p0 = 1, p1 = 0
+    values = np.zeros((1, 1, 64), np.int8)
+    meta = np.array([[[0x44444444, 0x44444441, 0x44444444, 0x44444444]]], np.uint32)  # p0 = 1, p1 = 0
     with pytest.raises(ValueError):
         oracle.decompress24(values, meta)
 
