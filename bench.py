@@ -13,6 +13,8 @@ The line also carries:
                MFMA peak; traffic from the committed rocprofv3 PMC record when
                it was taken on the current kernel source, else null;
   cpu_baseline the CPU oracle timed on this host on a bounded sample;
+  library_int_mm  the vendor library's int8 GEMM (torch._int_mm, hipBLASLt,
+               int32 out, no dequant) on the same inputs, for dense M > 16;
   decode_m16   the M=16 weight-streaming path (K=N=4096): GB/s of the GEMM
                kernel against HBM peak, with rotated weight copies so the
                256 MB Infinity Cache cannot serve them; the two-launch layer
@@ -305,6 +307,18 @@ def main():
     # the kernels alone: median of 5 regions of K calls each
     ms_gemm = time_median(gemm, args.steps, torch, R, args.eager)
     ms_quant = time_median(quant, args.steps, torch, R, args.eager)
+    # the vendor library on the same rotated inputs: torch._int_mm (hipBLASLt), int8 x int8
+    # -> int32 with no dequant epilogue (it writes 4 bytes per output, we write 2). Launched
+    # eagerly, never captured into a graph (a library call may record memsets); at tens of
+    # microseconds per call the launches still run back to back on the GPU.
+    library = None
+    if not bsr and not sp24 and M > 16:
+        ms_lib = time_median(lambda i: torch._int_mm(xqs[i % R], ws[i % R].t()), args.steps,
+                             torch, R, eager=True)
+        library = {"kernel": "torch._int_mm (hipBLASLt) int8 -> int32, no dequant epilogue",
+                   "us": round(ms_lib * 1e3, 3),
+                   "TOPs": round(2.0 * M * N * K / (ms_lib * 1e-3) / 1e12, 1),
+                   "w8a8_gemm_speedup": round(ms_lib / ms_gemm, 3)}
 
     ops = 2.0 * M * N * K
     if bsr:
@@ -365,6 +379,8 @@ def main():
     }
     if sp24:
         line["gemm_only"]["dense_equivalent_TOPs"] = round(2 * gemm_tops, 1)
+    if library is not None:
+        line["library_int_mm"] = library
     if not args.no_decode and name == "prefill_outliers":
         line["decode_m16"] = bench_decode(torch, np, b, dev, args.steps, args.warmup, args.eager)
     if not args.no_cpu_baseline:
