@@ -5,6 +5,7 @@ import this package. It shares nothing with the HIP library.
 """
 from .oracle import (  # noqa: F401
     build_oracle,
+    bf16_gemm,
     bf16_rne_from_f64,
     bsr_gemm_i32,
     compress24,
@@ -16,4 +17,5 @@ from .oracle import (  # noqa: F401
     num_threads,
     quantize_rows_bf16,
     quantize_rows_f32,
+    w4a16_dequant,
 )

@@ -59,6 +59,10 @@ def load_oracle():
     lib.oracle_compress24.restype = None
     lib.oracle_decompress24.argtypes = [p, p, i64, i64, p]
     lib.oracle_decompress24.restype = ctypes.c_int
+    lib.oracle_w4a16_dequant.argtypes = [p, p, p, i64, i64, i64, p]
+    lib.oracle_w4a16_dequant.restype = None
+    lib.oracle_bf16_gemm.argtypes = [p, p, i64, i64, i64, p]
+    lib.oracle_bf16_gemm.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -195,6 +199,35 @@ def decompress24(values: np.ndarray, meta: np.ndarray) -> np.ndarray:
     if load_oracle().oracle_decompress24(_ptr(values), _ptr(meta), N, K, _ptr(w)) != 0:
         raise ValueError("a group's positions are not p0 < p1")
     return w
+
+
+def w4a16_dequant(wq4: np.ndarray, scales: np.ndarray, zeros: np.ndarray) -> np.ndarray:
+    """Packed u4 [N,K/2] + bf16 scales/zeros [N,K/G] (bit patterns) -> bf16 w [N,K] (bits):
+    w = bf16(bf16(q - z) * s)."""
+    wq4 = _c(wq4, np.uint8)
+    scales = _c(scales, np.uint16)
+    zeros = _c(zeros, np.uint16)
+    N, K2 = wq4.shape
+    K = 2 * K2
+    if scales.shape != zeros.shape or scales.shape[0] != N or K % scales.shape[1]:
+        raise ValueError("W4A16 shapes")
+    G = K // scales.shape[1]
+    w = np.empty((N, K), np.uint16)
+    load_oracle().oracle_w4a16_dequant(_ptr(wq4), _ptr(scales), _ptr(zeros), N, K, G, _ptr(w))
+    return w
+
+
+def bf16_gemm(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """bf16 x [M,K] times bf16 w [N,K]^T, summed in float64, rounded once to bf16 (bits)."""
+    x_bits = _c(x_bits, np.uint16)
+    w_bits = _c(w_bits, np.uint16)
+    M, K = x_bits.shape
+    N, K2 = w_bits.shape
+    if K2 != K:
+        raise ValueError("inner dimensions")
+    out = np.empty((M, N), np.uint16)
+    load_oracle().oracle_bf16_gemm(_ptr(x_bits), _ptr(w_bits), M, N, K, _ptr(out))
+    return out
 
 
 def num_threads() -> int:

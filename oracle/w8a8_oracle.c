@@ -42,6 +42,15 @@
  *                (crow_indices / col_indices / values), pytorch/ao PR #821
  *                custom-op paragraph and the bsr_dense_addmm warning (Ms=64,
  *                Ks=64, beta=0, alpha=1).
+ *   W4A16:       asymmetric group-wise 4-bit weights with bf16 activations
+ *                (pytorch/ao PR #153, fused HQQ quantization GEMM: u4 weights
+ *                upcast to bf16, then group-wise scaling and shifting by the
+ *                scales and zero points, then the GEMM; quantization along K).
+ *                w[n,k] = bf16(bf16(q[n,k] - z[n,g]) * s[n,g]), g = k / G --
+ *                the elementwise bf16 arithmetic of that dequantization, each
+ *                operation rounded once to bf16 -- and
+ *                out[m,n] = bf16_rne(sum_k x[m,k] * w[n,k]), the products exact
+ *                and summed in float64, rounded once.
  *   2:4 weights: in every group of 4 consecutive weights along K at most two
  *                are kept -- the pages' cuSPARSELt route (Paddle PR #41770:
  *                sparse_fc on FC weights already pruned to 2:4, the
@@ -294,6 +303,50 @@ int oracle_decompress24(const int8_t *values, const uint32_t *meta, int64_t N, i
         }
     }
     return bad ? -1 : 0;
+}
+
+/* bf16 bit pattern -> float64 (exact). */
+static double bf16_to_f64(uint16_t bits) { return (double)bf16_bits_to_float(bits); }
+
+/*
+ * W4A16 dequantization. wq4 [N, K/2] bytes: byte j of row n holds q[n][2j] in
+ * its low nibble and q[n][2j+1] in its high nibble (u4, 0..15). scales, zeros:
+ * bf16 [N, K/G]. w [N,K] bf16 (bit patterns):
+ *   w[n][k] = bf16(bf16(q - z) * s),  s = scales[n][k/G], z = zeros[n][k/G].
+ * q - z and (q - z) * s are exact in float64 (at most 8 + 8 significant bits),
+ * so each bf16() is one rounding of the exact value.
+ */
+void oracle_w4a16_dequant(const uint8_t *wq4, const uint16_t *scales, const uint16_t *zeros,
+                          int64_t N, int64_t K, int64_t G, uint16_t *w) {
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            const uint8_t byte = wq4[n * (K / 2) + k / 2];
+            const int q = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+            const double s = bf16_to_f64(scales[n * (K / G) + k / G]);
+            const double z = bf16_to_f64(zeros[n * (K / G) + k / G]);
+            const double shifted = bf16_to_f64(oracle_bf16_rne_from_f64((double)q - z));
+            w[n * K + k] = oracle_bf16_rne_from_f64(shifted * s);
+        }
+    }
+}
+
+/*
+ * out[m][n] = bf16_rne(sum_k x[m][k] * w[n][k]) for bf16 x [M,K] and bf16 w [N,K]
+ * (bit patterns). Each product of two bf16 values is exact in float64; the
+ * float64 sum of K of them differs from the exact sum by far less than a bf16
+ * ulp of any result that is not itself a near-cancellation.
+ */
+void oracle_bf16_gemm(const uint16_t *x, const uint16_t *w, int64_t M, int64_t N, int64_t K,
+                      uint16_t *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) sum += bf16_to_f64(x[m * K + k]) * bf16_to_f64(w[n * K + k]);
+            out[m * N + n] = oracle_bf16_rne_from_f64(sum);
+        }
+    }
 }
 
 /* Threads the OpenMP loops above run on (1 without OpenMP). */

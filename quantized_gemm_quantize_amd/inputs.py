@@ -137,6 +137,49 @@ def make_linear(M: int, N: int, K: int, seed: int = 0, outlier_frac: float = 0.0
                         meta=meta)
 
 
+# W4A16 layers (pytorch/ao PR #153 benchmark shapes: M = 16 .. 1024 at N = K = 4096,
+# group size 128, bf16 activations, scales and zeros).
+W4A16_CONFIGS = {
+    "w4a16_decode": dict(M=16, K=4096, N=4096, G=128),
+    "w4a16": dict(M=1024, K=4096, N=4096, G=128),
+}
+W4A16_M = [16, 32, 128, 256, 512, 1024]
+
+
+@dataclass
+class W4A16Inputs:
+    """One synthetic W4A16 layer: bf16 X, packed u4 weights, bf16 group scales and zeros."""
+    x_bits: np.ndarray       # uint16 [M,K], bf16 bit patterns
+    wq4: np.ndarray          # uint8 [N,K/2]: q[n,2j] in the low nibble of byte j, q[n,2j+1] high
+    scales: np.ndarray       # uint16 [N,K/G], bf16 bit patterns
+    zeros: np.ndarray        # uint16 [N,K/G], bf16 bit patterns
+    G: int
+
+
+def pack_u4(q: np.ndarray) -> np.ndarray:
+    """u4 codes [N,K] -> bytes [N,K/2], even columns in the low nibble (bit placement only)."""
+    q = np.asarray(q, np.uint8)
+    return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+
+
+def make_w4a16(M: int, N: int, K: int, G: int = 128, seed: int = 0) -> W4A16Inputs:
+    """X ~ N(0,1) (bf16), u4 codes uniform on 0..15, scales uniform on [0.004, 0.012) and
+    zero points uniform on [6, 9) (both rounded to bf16): the magnitudes of a 4-bit group
+    quantization of N(0, 0.02) weights. Draw order: X, codes, scales, zeros."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    scales = rng.uniform(0.004, 0.012, size=(N, K // G)).astype(np.float32)
+    zeros = rng.uniform(6.0, 9.0, size=(N, K // G)).astype(np.float32)
+    return W4A16Inputs(x_bits=f32_to_bf16_bits(x), wq4=pack_u4(q), scales=f32_to_bf16_bits(scales),
+                       zeros=f32_to_bf16_bits(zeros), G=G)
+
+
+def make_w4a16_inputs(name: str, seed: int = 0, M: int | None = None) -> W4A16Inputs:
+    cfg = W4A16_CONFIGS[name]
+    return make_w4a16(M if M is not None else cfg["M"], cfg["N"], cfg["K"], cfg["G"], seed)
+
+
 def bsr_from_dense(w_dense: np.ndarray, block_mask: np.ndarray, bs: int):
     """Gather the kept bs x bs blocks of a dense [N,K] array into BSR arrays.
 

@@ -414,3 +414,69 @@ def test_sparse24_product_matches_float64_matmul(oracle):
     acc = oracle.gemm_i32(xq, oracle.decompress24(*oracle.compress24(wq)))
     ref = xq.astype(np.float64) @ wq.astype(np.float64).T
     assert np.array_equal(acc.astype(np.float64), ref)
+
+
+# --- W4A16 (asymmetric group-wise 4-bit weights, bf16 activations) ----------
+
+def _bits(h):
+    return np.array([int(h, 16)], np.uint16)
+
+
+def test_w4a16_dequant_hand_worked(oracle):
+    g = _load("w4a16_worked.json")
+    c = g["nibbles"]
+    w = oracle.w4a16_dequant(np.array([c["bytes"]], np.uint8), _bits(c["scale_bits"])[None, :],
+                             _bits(c["zero_bits"])[None, :])
+    assert bf16_bits_to_f32(w)[0].tolist() == c["w"]
+    for case in ("rounding", "shift_rounding"):
+        c = g[case]
+        wq4 = np.array([[c["q"] | (c["q"] << 4)]], np.uint8)          # the same code twice
+        w = oracle.w4a16_dequant(wq4, _bits(c["scale_bits"])[None, :], _bits(c["zero_bits"])[None, :])
+        assert w[0].tolist() == [int(c["w_bits"], 16)] * 2, case
+        assert float(bf16_bits_to_f32(w)[0, 0]) == c["w"]
+
+
+def test_w4a16_dequant_matches_exact_rationals(oracle):
+    """Every dequantized weight of a random layer against bf16(bf16(q - z) * s) evaluated on
+    exact rationals with bf16 rounding written out (the exact module)."""
+    from quantized_gemm_quantize_amd.inputs import make_w4a16
+    inp = make_w4a16(1, 6, 256, G=128, seed=9)
+    w = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros)
+    q = np.empty((6, 256), np.int64)
+    q[:, 0::2] = inp.wq4 & 15
+    q[:, 1::2] = inp.wq4 >> 4
+    s = bf16_bits_to_f32(inp.scales)
+    z = bf16_bits_to_f32(inp.zeros)
+    for n in range(6):
+        for k in range(256):
+            sv, zv = Fraction(float(s[n, k // 128])), Fraction(float(z[n, k // 128]))
+            ref = exact_bf16(exact_bf16(int(q[n, k]) - zv) * sv)
+            assert Fraction(float(bf16_bits_to_f32(w[n:n + 1, k:k + 1])[0, 0])) == ref, (n, k)
+
+
+def test_bf16_gemm_matches_exact_sums(oracle):
+    """The bf16 product against the exact rational sum rounded once to bf16 (brute force)."""
+    rng = np.random.default_rng(5)
+    x = f32_to_bf16_bits(rng.standard_normal((3, 40)).astype(np.float32))
+    w = f32_to_bf16_bits((rng.standard_normal((4, 40)) * 0.05).astype(np.float32))
+    out = oracle.bf16_gemm(x, w)
+    xf, wf = bf16_bits_to_f32(x), bf16_bits_to_f32(w)
+    for m in range(3):
+        for n in range(4):
+            exact = sum(Fraction(float(xf[m, k])) * Fraction(float(wf[n, k])) for k in range(40))
+            got = Fraction(float(bf16_bits_to_f32(out[m:m + 1, n:n + 1])[0, 0]))
+            assert got == exact_bf16(exact), (m, n)
+
+
+def test_w4a16_dequant_group_boundaries(oracle):
+    """Each column takes the scale and zero of its own group: a layer whose groups differ
+    only in scale dequantizes to q - z times the right group's scale."""
+    N, K, G = 2, 256, 64
+    q = np.tile(np.arange(16, dtype=np.uint8), (N, K // 16))
+    from quantized_gemm_quantize_amd.inputs import pack_u4
+    scales = f32_to_bf16_bits(np.array([[1.0, 2.0, 4.0, 8.0], [0.5, 0.25, 0.125, 1.0]], np.float32))
+    zeros = f32_to_bf16_bits(np.full((N, K // G), 8.0, np.float32))
+    w = bf16_bits_to_f32(oracle.w4a16_dequant(pack_u4(q), scales, zeros))
+    s = bf16_bits_to_f32(scales)
+    expect = (q.astype(np.float32) - 8.0) * np.repeat(s, G, axis=1)   # exact: small integers x 2^k
+    assert np.array_equal(w, expect)
