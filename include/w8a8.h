@@ -216,6 +216,40 @@ w8a8_status w8a8_sparse24_gemm(const int8_t *xq, const float *x_scale, int64_t M
                                int64_t N, int64_t K, void *out, w8a8_out_dtype out_dtype,
                                void *stream);
 
+/*
+ * W4A16: asymmetric group-wise 4-bit weights with bf16 activations (pytorch/ao
+ * PR #153, fused HQQ quantization GEMM: u4 weights upcast to bf16, scaled and
+ * shifted group-wise by bf16 scales and zero points along K, then the GEMM).
+ *   wq4     [N, K/2] uint8: byte j of row n holds code q[n][2j] (0..15) in its
+ *           low nibble and q[n][2j+1] in its high nibble
+ *   scales, zeros [N, K/G] bf16 (bit patterns), G = group_size
+ *   w[n][k] = bf16(bf16(q[n][k] - zeros[n][k/G]) * scales[n][k/G])
+ *           (each operation rounded to nearest-even bf16, as elementwise bf16
+ *           arithmetic does)
+ * N a positive multiple of 16, K a positive multiple of 128, G a positive
+ * multiple of 32 dividing K; wq4, x, w and out 16-byte aligned, scales and
+ * zeros 2-byte aligned.
+ */
+
+/* Dequantized weights: w [N,K] bf16, bit-exact to the definition above (the
+ * standalone dequantization the pages list next to the fused kernel). */
+w8a8_status w4a16_dequant(const uint8_t *wq4, const void *scales, const void *zeros, int64_t N,
+                          int64_t K, int64_t group_size, void *w, void *stream);
+
+/* Largest M taken by w4a16_gemm. */
+#define W4A16_MAX_M 64
+
+/*
+ * Fused dequant GEMM: out[m][n] = bf16(sum_k x[m][k] * w[n][k]) with x bf16
+ * [M,K] row-major, out bf16 [M,N] row-major, the products accumulated in
+ * fp32 (within one bf16 ulp plus the fp32 summation error of the exact sum).
+ * The dequantized weights never leave the chip. 0 <= M <= W4A16_MAX_M.
+ * Errors: NULL, SHAPE, ALIGN, HIP.
+ */
+w8a8_status w4a16_gemm(const void *x, int64_t M, const uint8_t *wq4, const void *scales,
+                       const void *zeros, int64_t N, int64_t K, int64_t group_size, void *out,
+                       void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *w8a8_status_string(int status);
 

@@ -28,6 +28,7 @@ W8A8_OUT_BF16 = 0
 W8A8_OUT_I32 = 1
 W8A8_MAX_K = 133136
 W8A8_FUSED_MAX_M = 64
+W4A16_MAX_M = 64
 
 _lib = None
 
@@ -60,8 +61,11 @@ def load():
     lib.w8a8_fused_linear.argtypes = [p, i64, i64, p, p, i64, p, f32, f32, p, p]
     lib.w8a8_compress24.argtypes = [p, i64, i64, p, p, p]
     lib.w8a8_sparse24_gemm.argtypes = [p, p, i64, p, p, p, i64, i64, p, i32, p]
+    lib.w4a16_dequant.argtypes = [p, p, p, i64, i64, i64, p, p]
+    lib.w4a16_gemm.argtypes = [p, i64, p, p, p, i64, i64, i64, p, p]
     for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_gemm_addmm",
-               "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_compress24", "w8a8_sparse24_gemm"):
+               "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_compress24", "w8a8_sparse24_gemm",
+               "w4a16_dequant", "w4a16_gemm"):
         getattr(lib, fn).restype = i32
     lib.w8a8_status_string.argtypes = [i32]
     lib.w8a8_status_string.restype = ctypes.c_char_p
@@ -213,6 +217,44 @@ def w8a8_sparse24_gemm(xq, x_scale, values, meta, w_scale, out=None, out_dtype="
     out = _out(out, M, N, od, xq.device)
     _call("w8a8_sparse24_gemm", xq.data_ptr(), x_scale.data_ptr(), M, values.data_ptr(),
           meta.data_ptr(), w_scale.data_ptr(), N, K, out.data_ptr(), od, _stream_handle(stream))
+    return out
+
+
+def _w4a16_operands(wq4, scales, zeros):
+    _check_tensor(wq4, "wq4", torch.uint8, 2)
+    _check_tensor(scales, "scales", torch.bfloat16, 2)
+    _check_tensor(zeros, "zeros", torch.bfloat16, 2)
+    N, K2 = wq4.shape
+    K = 2 * K2
+    if scales.shape != zeros.shape or scales.shape[0] != N or scales.shape[1] == 0 \
+            or K % scales.shape[1]:
+        raise ValueError("W4A16 operand shapes")
+    return N, K, K // scales.shape[1]
+
+
+def w4a16_dequant(wq4, scales, zeros, out=None, stream=None):
+    """Packed u4 [N,K/2] + bf16 scales/zeros [N,K/G] -> bf16 w [N,K] = bf16(bf16(q - z) * s)."""
+    N, K, G = _w4a16_operands(wq4, scales, zeros)
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=wq4.device)
+    _check_tensor(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (N, K):
+        raise ValueError("out shape")
+    _call("w4a16_dequant", wq4.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K, G,
+          out.data_ptr(), _stream_handle(stream))
+    return out
+
+
+def w4a16_gemm(x, wq4, scales, zeros, out=None, stream=None):
+    """out [M,N] bf16 = x [M,K] bf16 times the dequantized W4 weights, fused (M <= 64)."""
+    _check_tensor(x, "x", torch.bfloat16, 2)
+    N, K, G = _w4a16_operands(wq4, scales, zeros)
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("operand shapes")
+    out = _out(out, M, N, _out_dtype("bf16"), x.device)
+    _call("w4a16_gemm", x.data_ptr(), M, wq4.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N,
+          K, G, out.data_ptr(), _stream_handle(stream))
     return out
 
 

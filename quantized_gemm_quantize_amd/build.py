@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libw8a8.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["quantize_rows.hip", "gemm_tiled.hip", "gemm_decode.hip", "bsr_gemm.hip", "sparse24.hip",
-           "w8a8_abi.hip"]
+           "w4a16.hip", "w8a8_abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -190,6 +190,45 @@ w8a8_status w8a8_sparse24_gemm(const int8_t *xq, const float *x_scale, int64_t M
                                                  static_cast<hipStream_t>(stream)));
 }
 
+// W4A16 shape rules shared by both entry points.
+static w8a8_status w4a16_shape(int64_t N, int64_t K, int64_t G) {
+    if (N <= 0 || N % 16 != 0 || K <= 0 || K % 128 != 0 || G <= 0 || G % 32 != 0 || K % G != 0 ||
+        N > INT_MAX / 2 || K > INT_MAX / 2 || N * K / 8 > (int64_t)UINT_MAX * 256 / 2)
+        return W8A8_ERR_SHAPE;
+    return W8A8_OK;
+}
+
+static bool misaligned2(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 1u) != 0; }
+
+w8a8_status w4a16_dequant(const uint8_t *wq4, const void *scales, const void *zeros, int64_t N,
+                          int64_t K, int64_t group_size, void *w, void *stream) {
+    if (w8a8_status s = w4a16_shape(N, K, group_size)) return s;
+    if (!wq4 || !scales || !zeros || !w) return W8A8_ERR_NULL;
+    if (misaligned(wq4) || misaligned(w) || misaligned2(scales) || misaligned2(zeros))
+        return W8A8_ERR_ALIGN;
+    return hip_status(w4a16::launch_dequant(wq4, static_cast<const uint16_t *>(scales),
+                                            static_cast<const uint16_t *>(zeros), (int)N, (int)K,
+                                            (int)group_size, static_cast<uint16_t *>(w),
+                                            static_cast<hipStream_t>(stream)));
+}
+
+w8a8_status w4a16_gemm(const void *x, int64_t M, const uint8_t *wq4, const void *scales,
+                       const void *zeros, int64_t N, int64_t K, int64_t group_size, void *out,
+                       void *stream) {
+    if (M < 0 || M > W4A16_MAX_M) return W8A8_ERR_SHAPE;
+    if (w8a8_status s = w4a16_shape(N, K, group_size)) return s;
+    if (M == 0) return W8A8_OK;
+    if (!x || !wq4 || !scales || !zeros || !out) return W8A8_ERR_NULL;
+    if (misaligned(x) || misaligned(wq4) || misaligned(out) || misaligned2(scales) ||
+        misaligned2(zeros))
+        return W8A8_ERR_ALIGN;
+    return hip_status(w4a16::launch_gemm(static_cast<const uint16_t *>(x), (int)M, wq4,
+                                         static_cast<const uint16_t *>(scales),
+                                         static_cast<const uint16_t *>(zeros), (int)N, (int)K,
+                                         (int)group_size, static_cast<uint16_t *>(out),
+                                         static_cast<hipStream_t>(stream)));
+}
+
 const char *w8a8_status_string(int status) {
     switch (status) {
         case W8A8_OK: return "ok";

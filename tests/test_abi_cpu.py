@@ -26,14 +26,15 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w ]+?\*?\s*\b(w8a8_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w ]+?\*?\s*\b((?:w8a8|w4a16)_\w+)\s*\(", text,
+                                 re.M)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_gemm_addmm",
                "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_compress24", "w8a8_sparse24_gemm",
-               "w8a8_status_string", "w8a8_last_hip_error"):
+               "w4a16_dequant", "w4a16_gemm", "w8a8_status_string", "w8a8_last_hip_error"):
         assert fn in names
 
 
@@ -46,6 +47,7 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert f"#define W8A8_MAX_K {binding.W8A8_MAX_K}" in text
     assert f"#define W8A8_FUSED_MAX_M {binding.W8A8_FUSED_MAX_M}" in text
+    assert f"#define W4A16_MAX_M {binding.W4A16_MAX_M}" in text
     assert 127 * 127 * binding.W8A8_MAX_K < 2 ** 31
     assert 127 * 127 * (binding.W8A8_MAX_K + 16) >= 2 ** 31
     for name in ("W8A8_ERR_NULL", "W8A8_ERR_SHAPE", "W8A8_ERR_ALIGN", "W8A8_ERR_K_OVERFLOW",
@@ -162,6 +164,32 @@ def test_sparse24_gemm_validation(lib):
         assert g(*args(**{k: 0})) == NULL, k
         assert g(*args(**{k: P + 8})) == ALIGN, k
     assert g(*args(M=0, xq=0, xs=0, out=0)) == OK
+
+
+def test_w4a16_validation(lib):
+    d, g = lib.w4a16_dequant, lib.w4a16_gemm
+    dargs = lambda **kw: [kw.get("wq", P), kw.get("s", P), kw.get("z", P), kw.get("N", 64),
+                          kw.get("K", 256), kw.get("G", 128), kw.get("w", P), None]
+    gargs = lambda **kw: [kw.get("x", P), kw.get("M", 16), kw.get("wq", P), kw.get("s", P),
+                          kw.get("z", P), kw.get("N", 64), kw.get("K", 256), kw.get("G", 128),
+                          kw.get("out", P), None]
+    for f, args in ((d, dargs), (g, gargs)):
+        assert f(*args(N=40)) == SHAPE                   # N % 16
+        assert f(*args(N=0)) == SHAPE
+        assert f(*args(K=192)) == SHAPE                  # K % 128
+        assert f(*args(G=48)) == SHAPE                   # G % 32
+        assert f(*args(G=96)) == SHAPE                   # K % G
+        assert f(*args(G=0)) == SHAPE
+        assert f(*args(wq=0)) == NULL
+        assert f(*args(wq=P + 8)) == ALIGN
+        assert f(*args(s=P + 1)) == ALIGN                # scales need 2-byte alignment
+        assert f(*args(z=0)) == NULL
+    assert d(*dargs(w=P + 4)) == ALIGN
+    assert g(*gargs(M=-1)) == SHAPE
+    assert g(*gargs(M=65)) == SHAPE                      # above W4A16_MAX_M
+    assert g(*gargs(x=P + 2)) == ALIGN
+    assert g(*gargs(out=0)) == NULL
+    assert g(*gargs(M=0, x=0, out=0)) == OK
 
 
 def test_bsr_validation(lib):

@@ -11,8 +11,9 @@ import numpy as np
 import pytest
 import torch
 
-from quantized_gemm_quantize_amd.inputs import (CONFIGS, bf16_bits_to_f32, bsr_from_dense,
-                                                make_inputs, make_linear)
+from quantized_gemm_quantize_amd.inputs import (CONFIGS, W4A16_M, bf16_bits_to_f32,
+                                                bsr_from_dense, make_inputs, make_linear,
+                                                make_w4a16)
 
 pytestmark = pytest.mark.gpu
 
@@ -469,6 +470,60 @@ def test_sparse24_empty(b):
     meta = torch.zeros((1, 32, 4), dtype=torch.int32, device=DEV)
     ws = torch.ones((32,), dtype=torch.float32, device=DEV)
     assert b.w8a8_sparse24_gemm(xq, xs, values, meta, ws).shape == (0, 32)
+
+
+# --- W4A16 (group-wise 4-bit weights, bf16 activations) ---------------------
+
+def _w4a16_dev(inp):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return (to_dev_bf16(inp.x_bits), t(inp.wq4),
+            t(inp.scales.view(np.int16)).view(torch.bfloat16),
+            t(inp.zeros.view(np.int16)).view(torch.bfloat16))
+
+
+@pytest.mark.parametrize("N,K,G", [(16, 128, 128), (48, 256, 32), (64, 512, 64), (32, 1024, 256),
+                                   (4096, 4096, 128)])
+def test_w4a16_dequant_bit_exact(b, oracle, N, K, G):
+    log(f"w4a16 dequant N={N} K={K} G={G}")
+    inp = make_w4a16(1, N, K, G, seed=N + K + G)
+    _, wq4, s, z = _w4a16_dev(inp)
+    got = bf16_bits(b.w4a16_dequant(wq4, s, z))
+    ref = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} weights differ, first {bad[:4].tolist()}"
+
+
+def _w4a16_case(b, oracle, inp, what):
+    """w4a16_gemm against the oracle: the exact sum of the bf16 products rounded once, with
+    |gpu - oracle| <= 1 bf16 ulp + K * 2^-24 * sum_k |x w| (fp32 accumulation)."""
+    x, wq4, s, z = _w4a16_dev(inp)
+    got = bf16_bits(b.w4a16_gemm(x, wq4, s, z))
+    w = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros)
+    ref = oracle.bf16_gemm(inp.x_bits, w)
+    g = bf16_bits_to_f32(got).astype(np.float64)
+    o = bf16_bits_to_f32(ref).astype(np.float64)
+    xa = np.abs(bf16_bits_to_f32(inp.x_bits).astype(np.float64))
+    wa = np.abs(bf16_bits_to_f32(w).astype(np.float64))
+    K = xa.shape[1]
+    bound = _bf16_ulp(np.maximum(np.abs(g), np.abs(o))) + K * 2.0 ** -24 * (xa @ wa.T)
+    excess = np.abs(g - o) - bound
+    assert (excess <= 0).all(), f"{what}: {int((excess > 0).sum())} outputs outside the bound"
+    ulps = ulp_distance(got, ref)
+    log(f"  {what}: max {int(ulps.max())} ulp, {float((ulps > 1).mean()):.2e} beyond 1 ulp")
+
+
+@pytest.mark.parametrize("M,N,K,G", [(1, 16, 128, 128), (5, 48, 256, 32), (16, 128, 4096, 128),
+                                     (17, 64, 640, 64), (33, 32, 1024, 256), (64, 96, 512, 128)])
+def test_w4a16_gemm_shapes(b, oracle, M, N, K, G):
+    log(f"w4a16 gemm M={M} N={N} K={K} G={G}")
+    _w4a16_case(b, oracle, make_w4a16(M, N, K, G, seed=M + N + K), f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M", [m for m in W4A16_M if m <= 64])
+def test_w4a16_gemm_workload(b, oracle, M):
+    """The pages' benchmark shapes (N = K = 4096, group 128)."""
+    log(f"w4a16 workload M={M}")
+    _w4a16_case(b, oracle, make_w4a16(M, 4096, 4096, 128, seed=0), f"M={M} N=K=4096")
 
 
 # --- block-sparse GEMM ------------------------------------------------------
