@@ -236,14 +236,13 @@ w8a8_status w8a8_sparse24_gemm(const int8_t *xq, const float *x_scale, int64_t M
 w8a8_status w4a16_dequant(const uint8_t *wq4, const void *scales, const void *zeros, int64_t N,
                           int64_t K, int64_t group_size, void *w, void *stream);
 
-/* Largest M taken by w4a16_gemm. */
-#define W4A16_MAX_M 64
-
 /*
  * Fused dequant GEMM: out[m][n] = bf16(sum_k x[m][k] * w[n][k]) with x bf16
  * [M,K] row-major, out bf16 [M,N] row-major, the products accumulated in
  * fp32 (within one bf16 ulp plus the fp32 summation error of the exact sum).
- * The dequantized weights never leave the chip. 0 <= M <= W4A16_MAX_M.
+ * The dequantized weights never leave the chip. M >= 0: M <= 64 streams the
+ * weights once (dequantized in registers); larger M takes LDS tiles, each
+ * tile dequantizing its weight columns once for all of its rows.
  * Errors: NULL, SHAPE, ALIGN, HIP.
  */
 w8a8_status w4a16_gemm(const void *x, int64_t M, const uint8_t *wq4, const void *scales,

@@ -28,7 +28,6 @@ W8A8_OUT_BF16 = 0
 W8A8_OUT_I32 = 1
 W8A8_MAX_K = 133136
 W8A8_FUSED_MAX_M = 64
-W4A16_MAX_M = 64
 
 _lib = None
 
@@ -246,7 +245,7 @@ def w4a16_dequant(wq4, scales, zeros, out=None, stream=None):
 
 
 def w4a16_gemm(x, wq4, scales, zeros, out=None, stream=None):
-    """out [M,N] bf16 = x [M,K] bf16 times the dequantized W4 weights, fused (M <= 64)."""
+    """out [M,N] bf16 = x [M,K] bf16 times the dequantized W4 weights, fused."""
     _check_tensor(x, "x", torch.bfloat16, 2)
     N, K, G = _w4a16_operands(wq4, scales, zeros)
     M = x.shape[0]

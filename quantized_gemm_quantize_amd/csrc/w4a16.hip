@@ -146,6 +146,183 @@ hipError_t launch_decode_mt(const uint16_t *x, int M, const uint8_t *wq4, const 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// LDS-tiled W4A16 GEMM for M > 64: BM x BN tile per workgroup of 4 wavefronts
+// (2 x 2, v_mfma_f32_32x32x16_bf16, weights first), K advancing 64 columns
+// per stage through two LDS stages. Activations move global -> LDS with
+// direct-to-LDS 16-byte loads; the weight codes of a stage are loaded into
+// registers one stage ahead, dequantized once per workgroup and written to
+// LDS as bf16, where every wavefront of the tile reads them (the dequant
+// arithmetic per weight is shared by the tile's BM rows). Rows of 64 bf16 are
+// 128 bytes, chunk c of row r at slot c ^ (r % 8) ^ ((r / 8) % 2), as in the
+// int8 kernel. Two stages of 2 x (BM + BN) x 128 bytes leave room for two
+// workgroups per CU, so one's dequantization overlaps the other's MFMAs.
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <int BM, int BN>
+__global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
+    const uint16_t *__restrict__ X, const uint8_t *__restrict__ wq4,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    uint16_t *__restrict__ out, int M, int N, int K, int G, int tiles_m, int tiles_n) {
+    constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+    constexpr int XS = BM * 8, WS = BN * 8, STAGE = XS + WS;   // 16-byte slots
+    constexpr int XLD = XS / 256;                              // activation loads per wavefront
+    constexpr int CODES = BN * 64 / 256;                       // weight codes per thread per stage
+    static_assert(CODES == 32 || CODES == 16, "16 or 8 bytes of codes per thread");
+    static_assert(WM * WN * 2 * 4 <= 2 * STAGE * 16, "bf16 tile fits in the stage buffers");
+    __shared__ uint4 lds[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles = tiles_m * tiles_n;
+    const int t = w8a8::xcd_contiguous(blockIdx.x, tiles);
+    constexpr int kGroup = 4;
+    const int per_group = kGroup * tiles_n;
+    const int first_m = (t / per_group) * kGroup;
+    const int gsize = min(tiles_m - first_m, kGroup);
+    const int m0 = (first_m + (t % per_group) % gsize) * BM;
+    const int n0 = ((t % per_group) / gsize) * BN;
+    const int nk = K / 64;
+
+    // activation loads: load l of this wavefront fills slots 64 (wave + 4 l) ..
+    const uint16_t *xsrc[XLD];
+    {
+        const int row = 8 * wave + (lane >> 3);
+        const int kc = (lane & 7) ^ swz(row);
+#pragma unroll
+        for (int l = 0; l < XLD; ++l) xsrc[l] = X + (int64_t)min(m0 + row + 32 * l, M - 1) * K + 8 * kc;
+    }
+    // weight codes: thread tid dequantizes columns [CODES * part, +CODES) of tile row wr
+    constexpr int PARTS = 64 / CODES;
+    const int wr = tid / PARTS, part = tid % PARTS;
+    const int64_t wn_row = min(n0 + wr, N - 1);
+    const uint8_t *wsrc = wq4 + wn_row * (K / 2) + part * (CODES / 2);
+    const uint16_t *ssrc = scales + wn_row * (K / G), *zsrc = zeros + wn_row * (K / G);
+
+    typedef uint32_t Codes[CODES / 8];
+    auto load_codes = [&](int j, Codes &c, float &s, float &z) {
+        const uint8_t *src = wsrc + 32 * j;
+        if constexpr (CODES == 32) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(src);
+            c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
+        } else {
+            const uint2 v = *reinterpret_cast<const uint2 *>(src);
+            c[0] = v.x; c[1] = v.y;
+        }
+        const int g = (64 * j + part * CODES) / G;
+        s = bf16_to_float(ssrc[g]);
+        z = bf16_to_float(zsrc[g]);
+    };
+    auto store_codes = [&](const Codes &c, float s, float z, uint4 *buf) {
+        uint4 *wb = buf + XS + wr * 8;
+        const int sw = swz(wr);
+#pragma unroll
+        for (int i = 0; i < CODES / 8; ++i) wb[(part * (CODES / 8) + i) ^ sw] = dequant8(c[i], s, z);
+    };
+    auto load_x = [&](int j, uint4 *buf) {
+#pragma unroll
+        for (int l = 0; l < XLD; ++l)
+            __builtin_amdgcn_global_load_lds((global_void *)(xsrc[l] + 64 * j),
+                                             (lds_void *)(buf + 64 * (wave + 4 * l)), 16, 0, 0);
+    };
+
+    const int frag_row = lane & 31, kh = lane >> 5;
+    const int fswz = swz(frag_row);
+    v16f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
+    auto compute = [&](const uint4 *buf) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = (2 * u + kh) ^ fswz;
+            v8bf xa[TM], wb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                xa[i] = __builtin_bit_cast(v8bf, buf[(wm * WM + 32 * i + frag_row) * 8 + c]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                wb[j] = __builtin_bit_cast(v8bf, buf[XS + (wn * WN + 32 * j + frag_row) * 8 + c]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[j], xa[i], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    uint4 *const b0 = lds, *const b1 = lds + STAGE;
+    // prologue: stage 0 in LDS (activations landed, weights dequantized), the
+    // codes of stage 1 in registers
+    Codes c1;
+    float s1, z1;
+    load_x(0, b0);
+    {
+        Codes c0;
+        float s0, z0;
+        load_codes(0, c0, s0, z0);
+        store_codes(c0, s0, z0, b0);
+    }
+    if (nk > 1) load_codes(1, c1, s1, z1);
+    __syncthreads();
+    for (int s = 0; s < nk; ++s) {
+        uint4 *cur = (s & 1) ? b1 : b0, *nxt = (s & 1) ? b0 : b1;
+        // nxt was last read in stage s - 1, before the barrier that ended it
+        if (s + 1 < nk) {
+            load_x(s + 1, nxt);
+            store_codes(c1, s1, z1, nxt);
+        }
+        if (s + 2 < nk) load_codes(s + 2, c1, s1, z1);
+        compute(cur);
+        __syncthreads();
+    }
+
+    // epilogue: tile (i, j), element r of a lane: activation row i*32 + lane%32
+    // of the wavefront's sub-tile, channel j*32 + 8*(r/4) + 4*kh + r%4; the
+    // wavefront's WM x WN bf16 sub-tile is staged in LDS (16-byte chunks of a
+    // row permuted by the row), then stored as whole 16-byte row pieces
+    constexpr int CH = WN / 8, PM = CH < 8 ? CH - 1 : 7;
+    uint2 *st8 = reinterpret_cast<uint2 *>(lds) + wave * (WM * WN / 4);
+    const int mw0 = m0 + wm * WM, nw0 = n0 + wn * WN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int ml = i * 32 + frag_row;
+                const v16f &a = acc[i][j];
+                const uint32_t lo = pack_bf16x2(a[4 * g], a[4 * g + 1]);
+                const uint32_t hi = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
+                st8[(ml * CH + ((j * 4 + g) ^ (ml & PM))) * 2 + kh] = make_uint2(lo, hi);
+            }
+    __syncthreads();
+    const uint4 *st16 = reinterpret_cast<const uint4 *>(st8);
+#pragma unroll
+    for (int it = 0; it < WM * CH / kWave; ++it) {
+        const int q = it * kWave + lane;
+        const int ml = q / CH, cc = q % CH;
+        const int m = mw0 + ml, n = nw0 + cc * 8;
+        if (m < M && n < N)
+            w8a8::store16_nt(out + (int64_t)m * N + n, st16[ml * CH + (cc ^ (ml & PM))]);
+    }
+}
+
+template <int BM, int BN>
+hipError_t launch_tiled(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
+                        const uint16_t *zeros, int N, int K, int G, uint16_t *out,
+                        hipStream_t stream) {
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    w4a16_tiled_kernel<BM, BN><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream>>>(
+        x, wq4, scales, zeros, out, M, N, K, G, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_dequant(const uint8_t *wq4, const uint16_t *scales, const uint16_t *zeros, int N,
@@ -165,8 +342,12 @@ hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *wq4, const uint1
         case 2: return launch_decode_mt<2>(x, M, wq4, scales, zeros, N, K, G, out, stream);
         case 3: return launch_decode_mt<3>(x, M, wq4, scales, zeros, N, K, G, out, stream);
         case 4: return launch_decode_mt<4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-        default: return hipErrorNotSupported;
+        default: break;
     }
+    // 128 x 128 tiles when they fill the chip, else 64 x 64
+    const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
+    if (t128 >= 256) return launch_tiled<128, 128>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    return launch_tiled<64, 64>(x, M, wq4, scales, zeros, N, K, G, out, stream);
 }
 
 }  // namespace w4a16

@@ -215,8 +215,9 @@ w8a8_status w4a16_dequant(const uint8_t *wq4, const void *scales, const void *ze
 w8a8_status w4a16_gemm(const void *x, int64_t M, const uint8_t *wq4, const void *scales,
                        const void *zeros, int64_t N, int64_t K, int64_t group_size, void *out,
                        void *stream) {
-    if (M < 0 || M > W4A16_MAX_M) return W8A8_ERR_SHAPE;
+    if (M < 0 || M > INT_MAX / 2) return W8A8_ERR_SHAPE;
     if (w8a8_status s = w4a16_shape(N, K, group_size)) return s;
+    if ((M + 63) / 64 > INT_MAX / ((N + 63) / 64)) return W8A8_ERR_SHAPE;  // grid.x
     if (M == 0) return W8A8_OK;
     if (!x || !wq4 || !scales || !zeros || !out) return W8A8_ERR_NULL;
     if (misaligned(x) || misaligned(wq4) || misaligned(out) || misaligned2(scales) ||

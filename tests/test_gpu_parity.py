@@ -493,16 +493,19 @@ def test_w4a16_dequant_bit_exact(b, oracle, N, K, G):
     assert bad.size == 0, f"{len(bad)} weights differ, first {bad[:4].tolist()}"
 
 
-def _w4a16_case(b, oracle, inp, what):
+def _w4a16_case(b, oracle, inp, what, rows=None):
     """w4a16_gemm against the oracle: the exact sum of the bf16 products rounded once, with
-    |gpu - oracle| <= 1 bf16 ulp + K * 2^-24 * sum_k |x w| (fp32 accumulation)."""
+    |gpu - oracle| <= 1 bf16 ulp + K * 2^-24 * sum_k |x w| (fp32 accumulation); on the
+    given rows only (the oracle computes them one by one) when rows is set."""
     x, wq4, s, z = _w4a16_dev(inp)
     got = bf16_bits(b.w4a16_gemm(x, wq4, s, z))
     w = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros)
-    ref = oracle.bf16_gemm(inp.x_bits, w)
+    x_bits = inp.x_bits if rows is None else inp.x_bits[rows]
+    got = got if rows is None else got[rows]
+    ref = oracle.bf16_gemm(x_bits, w)
     g = bf16_bits_to_f32(got).astype(np.float64)
     o = bf16_bits_to_f32(ref).astype(np.float64)
-    xa = np.abs(bf16_bits_to_f32(inp.x_bits).astype(np.float64))
+    xa = np.abs(bf16_bits_to_f32(x_bits).astype(np.float64))
     wa = np.abs(bf16_bits_to_f32(w).astype(np.float64))
     K = xa.shape[1]
     bound = _bf16_ulp(np.maximum(np.abs(g), np.abs(o))) + K * 2.0 ** -24 * (xa @ wa.T)
@@ -512,18 +515,26 @@ def _w4a16_case(b, oracle, inp, what):
     log(f"  {what}: max {int(ulps.max())} ulp, {float((ulps > 1).mean()):.2e} beyond 1 ulp")
 
 
-@pytest.mark.parametrize("M,N,K,G", [(1, 16, 128, 128), (5, 48, 256, 32), (16, 128, 4096, 128),
-                                     (17, 64, 640, 64), (33, 32, 1024, 256), (64, 96, 512, 128)])
+@pytest.mark.parametrize("M,N,K,G", [
+    # weight-streaming path (M <= 64)
+    (1, 16, 128, 128), (5, 48, 256, 32), (16, 128, 4096, 128), (17, 64, 640, 64),
+    (33, 32, 1024, 256), (64, 96, 512, 128),
+    # tiled path: 64 x 64 tiles (ragged M and N) and 128 x 128 tiles (256+ of them)
+    (65, 64, 128, 128), (100, 80, 384, 32), (130, 272, 1024, 64), (257, 528, 256, 128),
+    (2048, 2048, 256, 128), (1100, 4096, 128, 128),
+])
 def test_w4a16_gemm_shapes(b, oracle, M, N, K, G):
     log(f"w4a16 gemm M={M} N={N} K={K} G={G}")
     _w4a16_case(b, oracle, make_w4a16(M, N, K, G, seed=M + N + K), f"M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M", [m for m in W4A16_M if m <= 64])
+@pytest.mark.parametrize("M", W4A16_M)
 def test_w4a16_gemm_workload(b, oracle, M):
-    """The pages' benchmark shapes (N = K = 4096, group 128)."""
+    """The pages' benchmark shapes (N = K = 4096, group 128), all rows up to M = 64, sampled
+    rows above."""
     log(f"w4a16 workload M={M}")
-    _w4a16_case(b, oracle, make_w4a16(M, 4096, 4096, 128, seed=0), f"M={M} N=K=4096")
+    rows = None if M <= 64 else _sampled_rows(M, n=24)
+    _w4a16_case(b, oracle, make_w4a16(M, 4096, 4096, 128, seed=0), f"M={M} N=K=4096", rows)
 
 
 # --- block-sparse GEMM ------------------------------------------------------
