@@ -28,7 +28,8 @@ and not the Python binding's per-call host overhead. ms_per_step is one timed
 region of exactly --steps steps; the kernel-alone figures (gemm_only, the
 roofline's avg_launch_us, quantize_rows) are the median of five regions of
 --steps calls each. Other workloads: --config (the roofline is HBM-bound for
-the BSR kernel and for M <= 64).
+the BSR kernel and for M <= 64); --config w4a16 / w4a16_decode time the W4A16
+fused dequant GEMM (bf16 TFLOP/s) with the pages' M = 16 .. 1024 sweep.
 """
 from __future__ import annotations
 
@@ -57,7 +58,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="prefill_outliers",
                     choices=["tiny", "decode", "prefill_outliers", "large_m", "bsr", "bsr_fc2",
-                             "sparse24", "sparse24_decode"])
+                             "sparse24", "sparse24_decode", "w4a16", "w4a16_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -229,6 +230,106 @@ def bench_decode(torch, np, b, dev, steps, warmup, eager=False):
             "layer_bytes": layer_bytes, "weight_copies_rotated": R}
 
 
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def w4a16_cpu_baseline(inp, np):
+    """The CPU oracle (dequantization + float64-summed bf16 GEMM) on a bounded row sample."""
+    import oracle
+    M, K = inp.x_bits.shape
+    N = inp.wq4.shape[0]
+
+    def run(rows):
+        t0 = time.perf_counter()
+        w = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros)
+        oracle.bf16_gemm(inp.x_bits[:rows], w)
+        return time.perf_counter() - t0
+
+    probe = min(M, 8)
+    t_probe = run(probe)
+    rows = int(min(M, max(probe, probe * 15.0 / max(t_probe, 1e-6))))
+    t = run(rows)
+    return {"value": round(2.0 * rows * N * K / t / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the W4A16 layer (M={M}, N={N}, K={K}): "
+                      f"dequantization of the whole weight + float64-summed bf16 GEMM, "
+                      f"{t:.2f} s wall"}
+
+
+def bench_w4a16(args, torch, np, b, dev):
+    """W4A16 fused dequant GEMM (one launch per step) on the pages' N = K = 4096, group 128
+    layer; with the M = 16 .. 1024 sweep of the pages' table, fused against the unfused
+    route (w4a16_dequant, then the vendor library's bf16 matmul)."""
+    from quantized_gemm_quantize_amd.inputs import W4A16_CONFIGS, W4A16_M, make_w4a16
+
+    cfg = W4A16_CONFIGS[args.config]
+    N, K, G = cfg["N"], cfg["K"], cfg["G"]
+    w_bytes = N * K // 2 + 2 * 2 * N * (K // G)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def setup(M):
+        inp = make_w4a16(M, N, K, G, seed=0)
+        R = rotation(w_bytes + 2 * M * K + 2 * M * N)
+        x = t(inp.x_bits.view(np.int16)).view(torch.bfloat16)
+        ws = [(t(inp.wq4), t(inp.scales.view(np.int16)).view(torch.bfloat16),
+               t(inp.zeros.view(np.int16)).view(torch.bfloat16)) for _ in range(R)]
+        outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        return inp, x, ws, outs, R
+
+    def fused_time(M, steps):
+        inp, x, ws, outs, R = setup(M)
+        fn = lambda i: b.w4a16_gemm(x, *ws[i % R], out=outs[i % R])
+        for i in range(max(args.warmup, R)):
+            fn(i)
+        return inp, time_median(fn, steps, torch, R, args.eager), R, x, ws
+
+    M = cfg["M"]
+    inp, ms, R, x, ws = fused_time(M, args.steps)
+    ms_step = time_loop(lambda i: b.w4a16_gemm(x, *ws[i % R]), args.steps, torch, period=R,
+                        eager=args.eager)
+    flops = 2.0 * M * N * K
+    value = flops / (ms_step * 1e-3) / 1e12
+    if M <= 64:
+        nbytes = 2 * M * K + w_bytes + 2 * M * N
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    else:
+        tf = flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    roof.update({"traffic": None, "kernel": "w4a16_gemm", "avg_launch_us": round(ms * 1e3, 3)})
+
+    sweep = []
+    for m in W4A16_M:
+        _, ms_f, Rm, xm, wsm = fused_time(m, max(50, args.steps // 4))
+        wbuf = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+
+        def unfused(i):
+            b.w4a16_dequant(*wsm[i % Rm], out=wbuf)
+            torch.matmul(xm, wbuf.t())
+        for i in range(5):
+            unfused(i)
+        ms_u = time_median(unfused, max(50, args.steps // 4), torch, Rm, eager=True)
+        sweep.append({"M": m, "fused_us": round(ms_f * 1e3, 3),
+                      "fused_TFLOPs": round(2.0 * m * N * K / (ms_f * 1e-3) / 1e12, 1),
+                      "unfused_us": round(ms_u * 1e3, 3)})
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "timing": "eager launches" if args.eager else "HIP graph replay",
+        "config": {"workload": f"{args.config} M={M} K={K} N={N} group={G}",
+                   "step": "w4a16_gemm", "seed": 0, "input_sets_rotated": R},
+        "roofline": roof,
+        "gemm_only": {"us": round(ms * 1e3, 3), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1)},
+        "sweep_n4096_k4096_g128": sweep,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = w4a16_cpu_baseline(inp, np)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -253,6 +354,9 @@ def main():
     b.load()
     dev = torch.device("cuda:0")
     name = args.config
+    if name.startswith("w4a16"):
+        bench_w4a16(args, torch, np, b, dev)
+        return
     d = prepare(name, torch, np, b, dev)
     inp = d["inp"]
     M, N, K = inp.M, inp.N, inp.K

@@ -149,35 +149,42 @@ hipError_t launch_decode_mt(const uint16_t *x, int M, const uint8_t *wq4, const 
 // ---------------------------------------------------------------------------
 // LDS-tiled W4A16 GEMM for M > 64: BM x BN tile per workgroup of 4 wavefronts
 // (2 x 2, v_mfma_f32_32x32x16_bf16, weights first), K advancing 64 columns
-// per stage through two LDS stages. Activations move global -> LDS with
-// direct-to-LDS 16-byte loads; the weight codes of a stage are loaded into
-// registers one stage ahead, dequantized once per workgroup and written to
-// LDS as bf16, where every wavefront of the tile reads them (the dequant
-// arithmetic per weight is shared by the tile's BM rows). Rows of 64 bf16 are
-// 128 bytes, chunk c of row r at slot c ^ (r % 8) ^ ((r / 8) % 2), as in the
-// int8 kernel. Two stages of 2 x (BM + BN) x 128 bytes leave room for two
-// workgroups per CU, so one's dequantization overlaps the other's MFMAs.
+// per stage. Activations move global -> LDS with direct-to-LDS 16-byte loads
+// through a ring of 4 stages (issued 3 stages ahead); the weight codes of a
+// stage are loaded into registers 2 stages ahead, dequantized once per
+// workgroup into one of two bf16 weight buffers in LDS a stage before they
+// are used, and read there by every wavefront of the tile (the dequant
+// arithmetic per weight is shared by the tile's BM rows). The dequantization
+// of stage s + 1 is interleaved with the MFMAs of stage s, so the vector ALU
+// and the matrix cores work at once. Rows of 64 bf16 are 128 bytes, chunk c of
+// row r at slot c ^ (r % 8) ^ ((r / 8) % 2), as in the int8 kernel. Barriers
+// wait only for the stage that must be complete (counted vector-memory waits,
+// no fence): loads of later stages stay in flight across them.
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
+template <int BM, int BN, int WAVES_M>
+__global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ X, const uint8_t *__restrict__ wq4,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     uint16_t *__restrict__ out, int M, int N, int K, int G, int tiles_m, int tiles_n) {
-    constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
-    constexpr int XS = BM * 8, WS = BN * 8, STAGE = XS + WS;   // 16-byte slots
+    constexpr int WAVES_N = 4 / WAVES_M;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 32, TN = WN / 32;
+    constexpr int XS = BM * 8, WS = BN * 8;                    // 16-byte slots per buffer
+    constexpr int XBUF = 4, WBUF = 2;
     constexpr int XLD = XS / 256;                              // activation loads per wavefront
     constexpr int CODES = BN * 64 / 256;                       // weight codes per thread per stage
+    constexpr int NLD = XLD + 3;                               // + codes, scale, zero
     static_assert(CODES == 32 || CODES == 16, "16 or 8 bytes of codes per thread");
-    static_assert(WM * WN * 2 * 4 <= 2 * STAGE * 16, "bf16 tile fits in the stage buffers");
-    __shared__ uint4 lds[2 * STAGE];
+    static_assert(WM * WN * 2 * 4 <= (XBUF * XS + WBUF * WS) * 16, "bf16 tile fits in LDS");
+    static_assert(TM >= 1 && TN >= 1 && 2 * NLD < 64, "wavefront tiles and the vmcnt range");
+    __shared__ uint4 lds[XBUF * XS + WBUF * WS];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int tiles = tiles_m * tiles_n;
     const int t = w8a8::xcd_contiguous(blockIdx.x, tiles);
     constexpr int kGroup = 4;
@@ -203,27 +210,31 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
     const uint8_t *wsrc = wq4 + wn_row * (K / 2) + part * (CODES / 2);
     const uint16_t *ssrc = scales + wn_row * (K / G), *zsrc = zeros + wn_row * (K / G);
 
-    typedef uint32_t Codes[CODES / 8];
-    auto load_codes = [&](int j, Codes &c, float &s, float &z) {
+    struct Codes {
+        uint32_t c[CODES / 8];
+        uint16_t s, z;
+    };
+    auto load_codes = [&](int j, Codes &c) {
         const uint8_t *src = wsrc + 32 * j;
         if constexpr (CODES == 32) {
             const uint4 v = *reinterpret_cast<const uint4 *>(src);
-            c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
+            c.c[0] = v.x; c.c[1] = v.y; c.c[2] = v.z; c.c[3] = v.w;
         } else {
             const uint2 v = *reinterpret_cast<const uint2 *>(src);
-            c[0] = v.x; c[1] = v.y;
+            c.c[0] = v.x; c.c[1] = v.y;
         }
         const int g = (64 * j + part * CODES) / G;
-        s = bf16_to_float(ssrc[g]);
-        z = bf16_to_float(zsrc[g]);
+        c.s = ssrc[g];
+        c.z = zsrc[g];
     };
-    auto store_codes = [&](const Codes &c, float s, float z, uint4 *buf) {
-        uint4 *wb = buf + XS + wr * 8;
-        const int sw = swz(wr);
-#pragma unroll
-        for (int i = 0; i < CODES / 8; ++i) wb[(part * (CODES / 8) + i) ^ sw] = dequant8(c[i], s, z);
+    auto xbuf = [&](int j) { return lds + (j % XBUF) * XS; };
+    auto wbuf = [&](int j) { return lds + XBUF * XS + (j % WBUF) * WS; };
+    // word i of a thread's codes, dequantized into its weight buffer slot
+    auto store_word = [&](const Codes &c, int i, uint4 *__restrict__ wb) {
+        wb[wr * 8 + ((part * (CODES / 8) + i) ^ swz(wr))] =
+            dequant8(c.c[i], bf16_to_float(c.s), bf16_to_float(c.z));
     };
-    auto load_x = [&](int j, uint4 *buf) {
+    auto load_x = [&](int j, uint4 *__restrict__ buf) {
 #pragma unroll
         for (int l = 0; l < XLD; ++l)
             __builtin_amdgcn_global_load_lds((global_void *)(xsrc[l] + 64 * j),
@@ -237,50 +248,86 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
-    auto compute = [&](const uint4 *buf) {
+    // the MFMAs on buffers xb, wb, with the dequantization of `next` into weight
+    // buffer `nb` interleaved between the 4 K steps
+    auto compute = [&](const uint4 *__restrict__ xb, const uint4 *__restrict__ wb,
+                       const Codes &next, uint4 *__restrict__ nb) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int c = (2 * u + kh) ^ fswz;
-            v8bf xa[TM], wb[TN];
+            v8bf xa[TM], wf[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                xa[i] = __builtin_bit_cast(v8bf, buf[(wm * WM + 32 * i + frag_row) * 8 + c]);
+                xa[i] = __builtin_bit_cast(v8bf, xb[(wm * WM + 32 * i + frag_row) * 8 + c]);
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                wb[j] = __builtin_bit_cast(v8bf, buf[XS + (wn * WN + 32 * j + frag_row) * 8 + c]);
+            for (int q = 0; q < TN; ++q)
+                wf[q] = __builtin_bit_cast(v8bf, wb[(wn * WN + 32 * q + frag_row) * 8 + c]);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[j], xa[i], acc[i][j], 0, 0, 0);
+                for (int q = 0; q < TN; ++q)
+                    acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[q], xa[i], acc[i][q], 0, 0, 0);
+            if (u < CODES / 8) store_word(next, u, nb);
         }
     };
 
-    uint4 *const b0 = lds, *const b1 = lds + STAGE;
-    // prologue: stage 0 in LDS (activations landed, weights dequantized), the
-    // codes of stage 1 in registers
-    Codes c1;
-    float s1, z1;
-    load_x(0, b0);
-    {
-        Codes c0;
-        float s0, z0;
-        load_codes(0, c0, s0, z0);
-        store_codes(c0, s0, z0, b0);
+    // The loop body is straight-line: stages past the last are loaded from the
+    // last stage (in bounds) into buffers that are never read again, and the
+    // last dequantization writes a weight buffer last read two stages earlier.
+    // So every barrier waits for a fixed count (the loads of the 2 stages issued
+    // after the one that must be complete) and the compiler's own waits before
+    // the dequantization are exact.
+    const int last = nk - 1;
+    // prologue: activations and codes of stages 0..2 in flight, stage 0
+    // dequantized; then stage 0 landed everywhere
+    Codes c0, c1, c2;
+    load_x(0, xbuf(0));
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(0, c0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(min(1, last), xbuf(1));
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(min(1, last), c1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(min(2, last), xbuf(2));
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(min(2, last), c2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < CODES / 8; ++i) store_word(c0, i, wbuf(0));
+    w8a8::vm_barrier<2 * NLD>();
+    // iteration s: issue stage s+3 (activations, codes into the registers that
+    // held stage s's codes, dequantized an iteration earlier), compute stage s
+    // while dequantizing stage s+1 (loaded two iterations earlier), then wait
+    // for stage s+1. Stage j's codes live in set j % 3; unrolling by 3 keeps
+    // that rotation free of register copies (a copy would wait for the load).
+    // The four buffers an iteration touches are distinct, and the restrict
+    // qualifiers say so: after inlining the accesses carry alias scopes, so the
+    // weight-buffer stores need not wait for the activation loads still landing
+    // in another buffer.
+    auto iteration = [&](int s, Codes &into, const Codes &deq, uint4 *__restrict__ xnew,
+                         const uint4 *__restrict__ xcur, const uint4 *__restrict__ wcur,
+                         uint4 *__restrict__ wnext) {
+        load_x(min(s + 3, last), xnew);
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(min(s + 3, last), into);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(xcur, wcur, deq, wnext);
+        w8a8::vm_barrier<2 * NLD>();
+    };
+#define W4A16_ITER(S, INTO, DEQ) \
+    iteration(S, INTO, DEQ, xbuf((S) + 3), xbuf(S), wbuf(S), wbuf((S) + 1))
+    int s = 0;
+    for (; s + 3 <= nk; s += 3) {
+        W4A16_ITER(s, c0, c1);
+        W4A16_ITER(s + 1, c1, c2);
+        W4A16_ITER(s + 2, c2, c0);
     }
-    if (nk > 1) load_codes(1, c1, s1, z1);
-    __syncthreads();
-    for (int s = 0; s < nk; ++s) {
-        uint4 *cur = (s & 1) ? b1 : b0, *nxt = (s & 1) ? b0 : b1;
-        // nxt was last read in stage s - 1, before the barrier that ended it
-        if (s + 1 < nk) {
-            load_x(s + 1, nxt);
-            store_codes(c1, s1, z1, nxt);
-        }
-        if (s + 2 < nk) load_codes(s + 2, c1, s1, z1);
-        compute(cur);
-        __syncthreads();
-    }
+    if (s < nk) { W4A16_ITER(s, c0, c1); ++s; }
+    if (s < nk) { W4A16_ITER(s, c1, c2); ++s; }
+#undef W4A16_ITER
+    // no load may still be landing in LDS when the epilogue reuses it
+    w8a8::vm_barrier<0>();
 
     // epilogue: tile (i, j), element r of a lane: activation row i*32 + lane%32
     // of the wavefront's sub-tile, channel j*32 + 8*(r/4) + 4*kh + r%4; the
@@ -313,12 +360,12 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
     }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WAVES_M>
 hipError_t launch_tiled(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
                         const uint16_t *zeros, int N, int K, int G, uint16_t *out,
                         hipStream_t stream) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    w4a16_tiled_kernel<BM, BN><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream>>>(
+    w4a16_tiled_kernel<BM, BN, WAVES_M><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream>>>(
         x, wq4, scales, zeros, out, M, N, K, G, tiles_m, tiles_n);
     return hipGetLastError();
 }
@@ -344,10 +391,13 @@ hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *wq4, const uint1
         case 4: return launch_decode_mt<4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
         default: break;
     }
-    // 128 x 128 tiles when they fill the chip, else 64 x 64
+    // 256 x 64 tiles (4 wavefronts along M: half the dequantization per output
+    // of 128 x 128) when they fill the chip, 128 x 128 next, else 64 x 64
+    const long t256 = (long)((M + 255) / 256) * ((N + 63) / 64);
     const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
-    if (t128 >= 256) return launch_tiled<128, 128>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-    return launch_tiled<64, 64>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    if (t256 >= 256) return launch_tiled<256, 64, 4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    if (t128 >= 256) return launch_tiled<128, 128, 2>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    return launch_tiled<64, 64, 2>(x, M, wq4, scales, zeros, N, K, G, out, stream);
 }
 
 }  // namespace w4a16
