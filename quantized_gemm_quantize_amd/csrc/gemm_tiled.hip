@@ -42,8 +42,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kBK = 128;          // K bytes per stage
-constexpr int kCPR = kBK / 16;    // 16-byte chunks per tile row
 // tile rows per group in the tile order (see the kernel): 4 for 256x128 tiles
 // (an XCD's 32 tiles then span 1024 rows x 1024 columns: less of A and B per
 // L2), 8 for 256x256
@@ -53,8 +51,18 @@ constexpr int group_m() { return BN == 128 ? 4 : 8; }
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 
-// bank-group swizzle of a 128-byte LDS row
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// Stages hold CPR 16-byte chunks of K per tile row (CPR = 8: 128 bytes of K,
+// CPR = 4: 64 bytes). Bank-group swizzle of such an LDS row: chunk c of row r
+// sits at slot c ^ swz<CPR>(r), so 8 and 16 consecutive rows reading the same
+// chunk hit distinct 16-byte bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+    static_assert(CPR == 8 || CPR == 4, "128- or 64-byte stage rows");
+    if constexpr (CPR == 8)
+        return (row & 7) ^ ((row >> 3) & 1);
+    else
+        return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+}
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt bits
 // [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima)
@@ -79,9 +87,10 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 // Per-lane load geometry of one tile: load l of this wavefront fills LDS slots
-// [wslot + 256 l, +64) (A) or [BM*kCPR + wslot + 256 l, +64) (B), i.e. tile
-// rows 8 wave + 32 l + lane/8 at physical slot lane % 8, which holds the
-// logical chunk kc = (lane % 8) ^ swz(row) -- the same for every l.
+// [wslot + 256 l, +64) (A) or [BM*CPR + wslot + 256 l, +64) (B), i.e. tile
+// rows (64/CPR) wave + (256/CPR) l + lane/CPR at physical slot lane % CPR,
+// which holds the logical chunk kc = (lane % CPR) ^ swz(row) -- the same for
+// every l.
 template <int A_LD, int B_LD>
 struct TileLoads {
     int aoff[A_LD], boff[B_LD];  // byte offsets of this lane's chunks in the tile rows
@@ -92,15 +101,15 @@ struct TileLoads {
 
 // Issue the direct-to-LDS loads of K stage j into `wr` (or, with KTAIL, zero
 // the slots whose chunk lies past K).
-template <int BM, int A_LD, int B_LD, bool KTAIL>
+template <int BM, int CPR, int A_LD, int B_LD, bool KTAIL>
 __device__ __forceinline__ void load_stage(const int8_t *__restrict__ at, const int8_t *__restrict__ bt,
                                            uint4 *__restrict__ wr, const TileLoads<A_LD, B_LD> &g,
                                            int j, int lane) {
-    const int k0 = j * kBK;
+    const int k0 = j * 16 * CPR;
     const bool in = !KTAIL || g.kc * 16 + k0 < g.K;
 #pragma unroll
     for (int l = 0; l < A_LD + B_LD; ++l) {
-        uint4 *dst = wr + g.wslot + (l < A_LD ? 256 * l : BM * kCPR + 256 * (l - A_LD));
+        uint4 *dst = wr + g.wslot + (l < A_LD ? 256 * l : BM * CPR + 256 * (l - A_LD));
         const int8_t *src = l < A_LD ? at + g.aoff[l] + k0 : bt + g.boff[l - A_LD] + k0;
         if (in)
             __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)dst, 16, 0, 0);
@@ -127,7 +136,7 @@ __device__ __forceinline__ void load_stage(const int8_t *__restrict__ at, const 
 // one direct-to-LDS load follows each further MFMA (this step's share of the
 // stage loads, steps 0-2). The order is pinned with scheduling barriers: a
 // wavefront issues in order, and a burst of loads would hold the MFMAs.
-template <int BM, int TM, int TN, int STAGES, int A_LD, int B_LD, bool KTAIL>
+template <int BM, int CPR, int TM, int TN, int STAGES, int A_LD, int B_LD, bool KTAIL>
 __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
                                                const int8_t *__restrict__ bt,
                                                const uint4 *__restrict__ rd, uint4 *__restrict__ wr,
@@ -139,12 +148,12 @@ __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
     constexpr int NLD = A_LD + B_LD;
     constexpr int NMF = TM * TN;        // MFMAs per K step
     constexpr int NRD = TM + TN;        // fragment reads per K step
-    constexpr int KS = kCPR / 2;        // K steps per stage
+    constexpr int KS = CPR / 2;         // K steps per stage
     constexpr int LPK = (NLD + KS - 2) / (KS - 1);  // loads per K step, steps 0..KS-2
     constexpr int NSLOT = NMF + 2 > NRD + LPK ? NMF + 2 : NRD + LPK;
     const int j_ahead = s + STAGES - 1;
     const bool ahead = j_ahead < g.nk;  // uniform
-    const int k0 = j_ahead * kBK;
+    const int k0 = j_ahead * 16 * CPR;
     const bool in = !KTAIL || g.kc * 16 + k0 < g.K;
     // with double buffering the next stage is the one being loaded into `wr`
     // (and `nx` is not accessed), otherwise it is `nx`
@@ -175,14 +184,14 @@ __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
                 for (int r = 0; r < NRD; ++r) {
                     if (r % 2 != q) continue;
                     if (r < TM)
-                        xa[f ^ 1][r] = __builtin_bit_cast(v4i, src_buf[a_frag + r * 32 * kCPR + ch]);
+                        xa[f ^ 1][r] = __builtin_bit_cast(v4i, src_buf[a_frag + r * 32 * CPR + ch]);
                     else
-                        wb[f ^ 1][r - TM] = __builtin_bit_cast(v4i, src_buf[b_frag + (r - TM) * 32 * kCPR + ch]);
+                        wb[f ^ 1][r - TM] = __builtin_bit_cast(v4i, src_buf[b_frag + (r - TM) * 32 * CPR + ch]);
                 }
             }
             const int l = kk * LPK + (q - 2);
             if (kk + 1 < KS && q >= 2 && q < 2 + LPK && l < NLD && ahead) {
-                uint4 *dst = wr + g.wslot + (l < A_LD ? 256 * l : BM * kCPR + 256 * (l - A_LD));
+                uint4 *dst = wr + g.wslot + (l < A_LD ? 256 * l : BM * CPR + 256 * (l - A_LD));
                 const int8_t *src = l < A_LD ? at + g.aoff[l] + k0 : bt + g.boff[l - A_LD] + k0;
                 if (in)
                     __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)dst, 16, 0, 0);
@@ -194,9 +203,9 @@ __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool KTAIL, bool OUT_I32,
-          bool ADDMM>
-__global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int CPR, int OCC, bool KTAIL,
+          bool OUT_I32, bool ADDMM>
+__global__ __launch_bounds__(kThreads, OCC) void gemm_tiled_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ sa, const int8_t *__restrict__ B,
     const float *__restrict__ sb, void *__restrict__ out, int M, int N, int K, int tiles_m,
     int tiles_n, Addmm am) {
@@ -205,10 +214,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
     static_assert(STAGES == 2 || STAGES == 3, "double or triple buffering");
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
-    // direct-to-LDS loads per wavefront per stage: each covers 8 tile rows
-    constexpr int A_LD = BM / (8 * kWaves), B_LD = BN / (8 * kWaves);
+    // direct-to-LDS loads per wavefront per stage: each covers 64/CPR tile rows
+    constexpr int A_LD = BM * CPR / (64 * kWaves), B_LD = BN * CPR / (64 * kWaves);
     constexpr int NLD = A_LD + B_LD;
-    constexpr int STAGE = (BM + BN) * kCPR;  // uint4 slots per stage
+    constexpr int STAGE = (BM + BN) * CPR;   // uint4 slots per stage
     static_assert(BM * BN * 2 <= STAGES * STAGE * 16, "bf16 tile fits in the stage buffers");
     __shared__ uint4 lds[STAGES * STAGE];
 
@@ -229,16 +238,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
 
     TileLoads<A_LD, B_LD> g;
     {
-        const int lrow = 8 * wave + (lane >> 3);
-        g.kc = (lane & 7) ^ swz(lrow);
+        const int lrow = (64 / CPR) * wave + lane / CPR;
+        g.kc = (lane % CPR) ^ swz<CPR>(lrow);
         const int a_last = min(BM, M - m0) - 1, b_last = min(BN, N - n0) - 1;
 #pragma unroll
-        for (int l = 0; l < A_LD; ++l) g.aoff[l] = min(lrow + 32 * l, a_last) * K + g.kc * 16;
+        for (int l = 0; l < A_LD; ++l) g.aoff[l] = min(lrow + (256 / CPR) * l, a_last) * K + g.kc * 16;
 #pragma unroll
-        for (int l = 0; l < B_LD; ++l) g.boff[l] = min(lrow + 32 * l, b_last) * K + g.kc * 16;
+        for (int l = 0; l < B_LD; ++l) g.boff[l] = min(lrow + (256 / CPR) * l, b_last) * K + g.kc * 16;
         g.wslot = 64 * wave;
         g.K = K;
-        g.nk = (K + kBK - 1) / kBK;
+        g.nk = (K + 16 * CPR - 1) / (16 * CPR);
     }
     const int nk = g.nk;
 
@@ -251,15 +260,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
     // fragment reads: lanes 0-31 take the first 16 bytes of each 32-byte K step,
     // lanes 32-63 the second, for both operands
     const int frag_row = lane & 31, half = lane >> 5;
-    const int a_frag = (wm * WM + frag_row) * kCPR;
-    const int b_frag = BM * kCPR + (wn * WN + frag_row) * kCPR;
-    const int fswz = swz(frag_row);
+    const int a_frag = (wm * WM + frag_row) * CPR;
+    const int b_frag = BM * CPR + (wn * WN + frag_row) * CPR;
+    const int fswz = swz<CPR>(frag_row);
     v4i xa[2][TM], wb[2][TN];
 
     uint4 *const b0 = lds, *const b1 = lds + STAGE, *const b2 = lds + (STAGES > 2 ? 2 : 0) * STAGE;
     // prologue: stages 0 .. STAGES-2 in flight, stage 0 landed everywhere
-    load_stage<BM, A_LD, B_LD, KTAIL>(at, bt, b0, g, 0, lane);
-    if (STAGES == 3 && nk > 1) load_stage<BM, A_LD, B_LD, KTAIL>(at, bt, b1, g, 1, lane);
+    load_stage<BM, CPR, A_LD, B_LD, KTAIL>(at, bt, b0, g, 0, lane);
+    if (STAGES == 3 && nk > 1) load_stage<BM, CPR, A_LD, B_LD, KTAIL>(at, bt, b1, g, 1, lane);
     if (STAGES == 3 && nk > 1)
         stage_barrier<NLD>();
     else
@@ -267,14 +276,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
     {
         const int ch0 = half ^ fswz;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) xa[0][i] = __builtin_bit_cast(v4i, b0[a_frag + i * 32 * kCPR + ch0]);
+        for (int i = 0; i < TM; ++i) xa[0][i] = __builtin_bit_cast(v4i, b0[a_frag + i * 32 * CPR + ch0]);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) wb[0][j] = __builtin_bit_cast(v4i, b0[b_frag + j * 32 * kCPR + ch0]);
+        for (int j = 0; j < TN; ++j) wb[0][j] = __builtin_bit_cast(v4i, b0[b_frag + j * 32 * CPR + ch0]);
     }
 
-#define W8A8_STAGE(RD, WR, NX, S_)                                                          \
-    mainloop_stage<BM, TM, TN, STAGES, A_LD, B_LD, KTAIL>(at, bt, RD, WR, NX, g, S_, lane, \
-                                                          a_frag, b_frag, half, fswz, acc, xa, wb)
+#define W8A8_STAGE(RD, WR, NX, S_)                                                               \
+    mainloop_stage<BM, CPR, TM, TN, STAGES, A_LD, B_LD, KTAIL>(at, bt, RD, WR, NX, g, S_, lane, \
+                                                               a_frag, b_frag, half, fswz, acc,  \
+                                                               xa, wb)
     int s = 0;
     if constexpr (STAGES == 3) {
         for (; s + 3 <= nk; s += 3) {
@@ -318,9 +328,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
         }
     } else {
         // stage the wave's WM x WN bf16 sub-tile in LDS (row-major, 16-byte
-        // chunks of a row permuted by row % 8), then store whole 16-byte pieces
+        // chunks of a row permuted by the low row bits, so that the 32 rows of
+        // one store instruction spread over all banks), then store whole
+        // 16-byte pieces
         constexpr int CH = WN / 8;  // 16-byte chunks per staged row
-        static_assert(CH >= 8, "the row-chunk permutation needs 8 chunks per row");
+        static_assert(CH == 8 || CH == 16, "the row-chunk permutation needs 8 or 16 chunks per row");
+        constexpr int PM = CH - 1;
         uint2 *st8 = reinterpret_cast<uint2 *>(lds) + wave * (WM * WN / 4);
         // per 4 channels: their scales (and bias) once, then the TM rows
         float sxv[TM];
@@ -344,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
                     const uint32_t hi =
                         pack_bf16x2(addmm<ADDMM>((float)a[4 * g + 2] * sxv[i] * w.z, am, bv.z),
                                     addmm<ADDMM>((float)a[4 * g + 3] * sxv[i] * w.w, am, bv.w));
-                    const int chunk = (j * 4 + g) ^ (ml & 7);
+                    const int chunk = (j * 4 + g) ^ (ml & PM);
                     st8[(ml * CH + chunk) * 2 + half] = make_uint2(lo, hi);
                 }
             }
@@ -355,40 +368,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(
             const int q = it * kWave + lane;
             const int ml = q / CH, cc = q % CH;
             const int m = mw0 + ml, n = nw0 + cc * 8;
-            const uint4 v = st16[ml * CH + (cc ^ (ml & 7))];
+            const uint4 v = st16[ml * CH + (cc ^ (ml & PM))];
             if (m < M && n < N)
                 store16_nt(static_cast<__bf16 *>(out) + (int64_t)m * N + n, v);
         }
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool KTAIL>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int CPR, int OCC, bool KTAIL>
 void launch_tail(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
                  int N, int K, void *out, bool out_i32, hipStream_t stream, const Addmm *am) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
     const Addmm a = am ? *am : Addmm{nullptr, 1.0f, 0.0f};
     if (out_i32)
-        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, KTAIL, true, false>
+        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, CPR, OCC, KTAIL, true, false>
             <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, tiles_m, tiles_n, a);
     else if (am)
-        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, KTAIL, false, true>
+        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, CPR, OCC, KTAIL, false, true>
             <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, tiles_m, tiles_n, a);
     else
-        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, KTAIL, false, false>
+        gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, CPR, OCC, KTAIL, false, false>
             <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, tiles_m, tiles_n, a);
 }
 
-// K % 128 != 0 takes the variant that zeroes the chunks past K.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+// K not a multiple of the stage depth takes the variant that zeroes the
+// chunks past K.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int CPR = 8, int OCC = 1>
 hipError_t launch_cfg(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
                       int N, int K, void *out, bool out_i32, hipStream_t stream, const Addmm *am) {
-    if (K % kBK == 0)
-        launch_tail<BM, BN, WAVES_M, WAVES_N, STAGES, false>(xq, xs, M, wq, ws, N, K, out, out_i32,
-                                                             stream, am);
+    if (K % (16 * CPR) == 0)
+        launch_tail<BM, BN, WAVES_M, WAVES_N, STAGES, CPR, OCC, false>(xq, xs, M, wq, ws, N, K, out,
+                                                                       out_i32, stream, am);
     else
-        launch_tail<BM, BN, WAVES_M, WAVES_N, STAGES, true>(xq, xs, M, wq, ws, N, K, out, out_i32,
-                                                            stream, am);
+        launch_tail<BM, BN, WAVES_M, WAVES_N, STAGES, CPR, OCC, true>(xq, xs, M, wq, ws, N, K, out,
+                                                                      out_i32, stream, am);
     return hipGetLastError();
 }
 
@@ -401,10 +415,16 @@ hipError_t launch_gemm_decode(const int8_t *xq, const float *xs, int M, const in
 hipError_t launch_gemm(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
                        int N, int K, void *out, bool out_i32, hipStream_t stream, const Addmm *am) {
     if (M <= 64) return launch_gemm_decode(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
-    // Enough 256x256 tiles to fill 256 CUs several times over: the big tile
-    // halves LDS traffic per MFMA. Otherwise 256x128 (or 128x128) tiles.
+    // Many tiles (enough 256x256 ones to fill 256 CUs four times over): with
+    // K up to 1024, two 256x128 workgroups per CU (64-byte K stages, 72 KB of
+    // LDS and at most 256 registers each), so that one tile's prologue and
+    // epilogue run beside the other's MFMAs; with longer K, 256x256 tiles,
+    // which halve the LDS traffic per MFMA. Otherwise 256x128 (or 128x128)
+    // tiles, one workgroup per CU.
     const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
     const long t128 = (long)((M + 255) / 256) * ((N + 127) / 128);
+    if (t256 >= 4 * 256 && K <= 1024)
+        return launch_cfg<256, 128, 2, 2, 3, 4, 2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
     if (t256 >= 4 * 256) return launch_cfg<256, 256, 2, 2, 2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
     if (t128 >= 256) return launch_cfg<256, 128, 2, 2, 3>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
     return launch_cfg<128, 128, 2, 2, 2>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);

@@ -222,6 +222,30 @@ def test_gemm_workloads_full_size(b, oracle, name):
     assert np.isfinite(bf16_bits_to_f32(out)).all()
 
 
+# Shapes with over a thousand 256x256 output tiles: K <= 1024 takes 256x128
+# tiles at two workgroups per CU (64-byte K stages), longer K 256x256 tiles.
+# K shorter than the stage ring, K a multiple of the stage, and ragged K, M
+# and N. Rows sampled in every 256-row tile, all columns.
+BIG_TILE_SHAPES = [(8300, 8208, 80), (8192, 8192, 320), (8200, 8256, 1008), (8256, 8208, 1040),
+                   (8192, 8192, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", BIG_TILE_SHAPES)
+def test_gemm_big_tiles(b, oracle, M, N, K):
+    log(f"gemm big tiles M={M} N={N} K={K}")
+    inp = make_linear(M, N, K, seed=M + N + K)
+    xq, sx, xq_ref, sx_ref = _check_quantize(b, oracle, inp.x_bits, f"M={M} N={N} K={K}")
+    wq, sw, wq_ref, sw_ref = gpu_weights(b, oracle, inp.w)
+    acc = b.w8a8_gemm(xq, sx, wq, sw, out_dtype="i32").cpu().numpy()
+    out = bf16_bits(b.w8a8_gemm(xq, sx, wq, sw))
+    rows = np.unique(np.concatenate([np.arange(0, M, 127), np.arange(M - 3, M)]))
+    acc_ref = oracle.gemm_i32(xq_ref[rows], wq_ref)
+    bad = np.argwhere(acc[rows] != acc_ref)
+    assert bad.size == 0, f"int32 acc differs at {len(bad)} places, first {bad[:4].tolist()}"
+    out_ref = oracle.epilogue_bf16(acc_ref, sx_ref[rows], sw_ref)
+    assert_bf16_close(out[rows], out_ref, f"M={M} N={N} K={K}")
+
+
 def test_gemm_deterministic(b, oracle):
     log("gemm determinism")
     inp = make_inputs("prefill_outliers", M=512)
