@@ -176,6 +176,24 @@ w8a8_status w8a8_bsr_gemm(const int8_t *xq, const float *x_scale, int64_t M, int
                           w8a8_out_dtype out_dtype, void *stream);
 
 /*
+ * Block-sparse (BSR) W8A8 GEMM with the addmm epilogue of w8a8_gemm_addmm
+ * (bf16 output) -- bsr_dense_addmm's own form (pytorch/ao PR #821, the
+ * warning's "beta=0 alpha=1"), here with any finite alpha and beta and a
+ * per-output-channel fp32 bias [N]:
+ *   out[m,n] = bf16_rne(alpha * (acc * x_scale[m] * w_scale[n]) + beta * bias[n])
+ * Block rows with no stored block have acc = 0 and write bf16(beta * bias[n])
+ * (+0 or -0 without a bias). bias may be NULL when beta == 0. Other arguments
+ * as w8a8_bsr_gemm.
+ * Errors: NULL (also bias NULL with beta != 0), SHAPE, K_OVERFLOW, BLOCKSIZE,
+ *         ALIGN (bias included), VALUE (alpha or beta not finite), HIP.
+ */
+w8a8_status w8a8_bsr_gemm_addmm(const int8_t *xq, const float *x_scale, int64_t M, int64_t K,
+                                const int32_t *crow, const int32_t *col, const int8_t *values,
+                                int64_t nnzb, int64_t bs, const float *w_scale, int64_t N,
+                                const float *bias, float alpha, float beta, void *out,
+                                void *stream);
+
+/*
  * 2:4 semi-structured weights (the pages' cuSPARSELt route: Paddle sparse_fc
  * PR #41770 runs FC weights already pruned to 2:4 -- at most two nonzeros in
  * every group of 4 consecutive weights along K -- and pytorch/ao PR #821 wants

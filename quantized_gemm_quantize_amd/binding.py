@@ -57,13 +57,16 @@ def load():
     lib.w8a8_bsr_gemm.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, p, i32, p]
     f32 = ctypes.c_float
     lib.w8a8_gemm_addmm.argtypes = [p, p, i64, p, p, i64, i64, p, f32, f32, p, p]
+    lib.w8a8_bsr_gemm_addmm.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, p, f32, f32,
+                                        p, p]
     lib.w8a8_fused_linear.argtypes = [p, i64, i64, p, p, i64, p, f32, f32, p, p]
     lib.w8a8_compress24.argtypes = [p, i64, i64, p, p, p]
     lib.w8a8_sparse24_gemm.argtypes = [p, p, i64, p, p, p, i64, i64, p, i32, p]
     lib.w4a16_dequant.argtypes = [p, p, p, i64, i64, i64, p, p]
     lib.w4a16_gemm.argtypes = [p, i64, p, p, p, i64, i64, i64, p, p]
     for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_gemm_addmm",
-               "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_compress24", "w8a8_sparse24_gemm",
+               "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_bsr_gemm_addmm", "w8a8_compress24",
+               "w8a8_sparse24_gemm",
                "w4a16_dequant", "w4a16_gemm"):
         getattr(lib, fn).restype = i32
     lib.w8a8_status_string.argtypes = [i32]
@@ -276,6 +279,34 @@ def w8a8_bsr_gemm(xq, x_scale, crow, col, values, w_scale, out=None, out_dtype="
     _call("w8a8_bsr_gemm", xq.data_ptr(), x_scale.data_ptr(), M, K, crow.data_ptr(),
           col.data_ptr() if nnzb else 0, values.data_ptr() if nnzb else 0, nnzb, bs,
           w_scale.data_ptr(), N, out.data_ptr(), od, _stream_handle(stream))
+    return out
+
+
+def w8a8_bsr_gemm_addmm(xq, x_scale, crow, col, values, w_scale, bias=None, alpha=1.0, beta=1.0,
+                        out=None, stream=None):
+    """Block-sparse W8A8 GEMM with the addmm epilogue (bf16 out):
+    out = bf16(alpha * (acc * x_scale[m] * w_scale[n]) + beta * bias[n]); bias None
+    (allowed with beta == 0) means no bias term."""
+    _check_tensor(xq, "xq", torch.int8, 2)
+    _check_tensor(x_scale, "x_scale", torch.float32, 1)
+    _check_tensor(crow, "crow", torch.int32, 1)
+    _check_tensor(col, "col", torch.int32, 1)
+    _check_tensor(values, "values", torch.int8, 3)
+    _check_tensor(w_scale, "w_scale", torch.float32, 1)
+    M, K = xq.shape
+    nnzb, bs, bs2 = values.shape
+    N = w_scale.shape[0]
+    if bs != bs2 or col.shape[0] != nnzb or crow.shape[0] != N // max(bs, 1) + 1:
+        raise ValueError("BSR array shapes")
+    if bias is not None:
+        _check_tensor(bias, "bias", torch.float32, 1)
+        if tuple(bias.shape) != (N,):
+            raise ValueError("bias shape")
+    out = _out(out, M, N, _out_dtype("bf16"), xq.device)
+    _call("w8a8_bsr_gemm_addmm", xq.data_ptr(), x_scale.data_ptr(), M, K, crow.data_ptr(),
+          col.data_ptr() if nnzb else 0, values.data_ptr() if nnzb else 0, nnzb, bs,
+          w_scale.data_ptr(), N, None if bias is None else bias.data_ptr(), float(alpha),
+          float(beta), out.data_ptr(), _stream_handle(stream))
     return out
 
 

@@ -37,6 +37,11 @@
 //    the ~8 block rows that read one X block find it in that XCD's L2, and
 //    their stores land in adjacent 128-byte pieces of the same output rows
 //    (scattered 128-byte pieces cost the write path about 10%);
+//  - the addmm variant (alpha, beta, a per-channel bias) reads the tile's 64
+//    bias values with scalar loads in the consumers' epilogue: no LDS (the
+//    budget of two workgroups per CU is spent) and no vector-memory wait in
+//    the consumers; block rows without stored blocks then write
+//    bf16(alpha * 0 + beta * bias[n]) through the same epilogue;
 //  - measured and not kept: 8 consumers of 32 rows each
 //    (more store streams, but more barrier and LDS traffic) and equal-work
 //    contiguous tile runs (better balance, scattered stores).
@@ -95,6 +100,7 @@ typedef __attribute__((address_space(4))) const int32_t const_i32;
 __device__ __forceinline__ int load_index(const int32_t *p, int i) {
     return ((const_i32 *)p)[i];
 }
+typedef __attribute__((address_space(4))) const float const_f32;
 
 struct Args {
     const int8_t *A;
@@ -104,6 +110,7 @@ struct Args {
     const float *sb;
     void *out;
     int nnzb, M, N, K, block_rows;
+    Addmm am;  // used by the addmm variant only
 };
 
 // The tiles of one workgroup: lo, lo + step, ... < hi. Tile t is X slab
@@ -245,11 +252,15 @@ __device__ __forceinline__ void store_zero_rows(const Args &a, int m0, int br, i
 // into the private staging rows (16-byte chunk c of row r at slot
 // c ^ oswz(r)), read it back as 16-byte pieces, 8 lanes per row, and store.
 // Half-line (64-byte) pieces cost the write path about half its rate.
-template <typename OutT>
+//
+// ADDMM: out = bf16(alpha * (acc * sa * sb) + beta * bias[n]). EMPTY (addmm
+// only): a block row without stored blocks, acc = 0 and no ring buffer.
+template <typename OutT, bool ADDMM, bool EMPTY>
 __device__ __forceinline__ void store_tile(const Args &a, const uint4 *__restrict__ buf,
                                            uint4 *__restrict__ stg, const v16i (&acc)[kTM][2],
                                            int m0, int br, int w, int lane) {
     constexpr bool kI32 = std::is_same<OutT, int32_t>::value;
+    static_assert(!(kI32 && ADDMM) && (ADDMM || !EMPTY), "addmm writes bf16");
     constexpr int kCp = 128 / (int)sizeof(OutT);  // channels per 128-byte row piece
     constexpr int kPieces = kBS / kCp;            // pieces per row: 1 (bf16) or 2 (int32)
     const int frag_row = lane & 31, half = lane >> 5;
@@ -257,12 +268,27 @@ __device__ __forceinline__ void store_tile(const Args &a, const uint4 *__restric
     const float *sa_l = reinterpret_cast<const float *>(buf + kSaOff);
     const float *sb_l = reinterpret_cast<const float *>(buf + kSbOff);
     char *sbytes = reinterpret_cast<char *>(stg);
+    // addmm: the tile's 64 bias values are uniform, read once per tile with
+    // scalar loads into ub (uniform registers); each lane selects its own
+    // 4 channels 32 jt + 8 g + 4 half + (0..3) where it uses them.
+    // (readfirstlane keeps the compiler from turning the select of two loads
+    // into one vector load, whose wait would also wait for this wavefront's
+    // output stores.)
+    float ub[kBS];
+#pragma unroll
+    for (int c = 0; c < kBS; ++c) ub[c] = 0.0f;
+    if (ADDMM && a.am.bias) {
+        const const_f32 *bb = (const const_f32 *)(a.am.bias + br * kBS);
+#pragma unroll
+        for (int c = 0; c < kBS; ++c)
+            ub[c] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, bb[c])));
+    }
 #pragma unroll
     for (int rg = 0; rg < kRowsPerMath / kSR; ++rg) {
         const int i = rg * kSR / 32;  // MFMA row tile of this pass
         // with 16-row passes, half of the lanes hold the pass's rows
         const bool mine = kSR == 32 || (frag_row >> 4) == (rg & 1);
-        const float sx = kI32 ? 0.0f : sa_l[kRowsPerMath * w + 32 * i + frag_row];
+        const float sx = kI32 || EMPTY ? 0.0f : sa_l[kRowsPerMath * w + 32 * i + frag_row];
 #pragma unroll
         for (int h = 0; h < kPieces; ++h) {
             if (mine) {
@@ -279,11 +305,17 @@ __device__ __forceinline__ void store_tile(const Args &a, const uint4 *__restric
                                 v4i{acc[i][jt][4 * g], acc[i][jt][4 * g + 1], acc[i][jt][4 * g + 2],
                                     acc[i][jt][4 * g + 3]};
                         } else {
-                            const float4 s = *reinterpret_cast<const float4 *>(sb_l + c0);
-                            const uint32_t lo = pack_bf16x2((float)acc[i][jt][4 * g] * sx * s.x,
-                                                            (float)acc[i][jt][4 * g + 1] * sx * s.y);
-                            const uint32_t hi = pack_bf16x2((float)acc[i][jt][4 * g + 2] * sx * s.z,
-                                                            (float)acc[i][jt][4 * g + 3] * sx * s.w);
+                            const float4 s = EMPTY ? make_float4(0.0f, 0.0f, 0.0f, 0.0f)
+                                                   : *reinterpret_cast<const float4 *>(sb_l + c0);
+                            const int cb = 32 * jt + 8 * g;
+                            const float4 bv = half ? make_float4(ub[cb + 4], ub[cb + 5], ub[cb + 6], ub[cb + 7])
+                                                   : make_float4(ub[cb], ub[cb + 1], ub[cb + 2], ub[cb + 3]);
+                            const uint32_t lo =
+                                pack_bf16x2(addmm<ADDMM>((float)acc[i][jt][4 * g] * sx * s.x, a.am, bv.x),
+                                            addmm<ADDMM>((float)acc[i][jt][4 * g + 1] * sx * s.y, a.am, bv.y));
+                            const uint32_t hi =
+                                pack_bf16x2(addmm<ADDMM>((float)acc[i][jt][4 * g + 2] * sx * s.z, a.am, bv.z),
+                                            addmm<ADDMM>((float)acc[i][jt][4 * g + 3] * sx * s.w, a.am, bv.w));
                             *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
                         }
                     }
@@ -331,7 +363,7 @@ __device__ __forceinline__ void multiply_block(const uint4 *buf, int w, int frag
 
 // The consumers' share of one segment: multiply each tile's blocks as they
 // land (one barrier per block), then scale and store the tile.
-template <typename OutT>
+template <typename OutT, bool ADDMM>
 __device__ __forceinline__ void consumer(const Args &a, uint4 *lds, const int2 *meta,
                                          const TileList &L, int s0, int cnt, int w, int lane) {
     const int frag_row = lane & 31, half = lane >> 5;
@@ -343,7 +375,14 @@ __device__ __forceinline__ void consumer(const Args &a, uint4 *lds, const int2 *
         const int2 r = meta[k];
         const int j0 = r.x, j1 = r.y;
         if (j0 == j1) {
-            store_zero_rows<OutT>(a, m0, br, w, lane);
+            if constexpr (ADDMM) {
+                v16i zero[kTM][2];
+#pragma unroll
+                for (int i = 0; i < kTM; ++i) zero[i][0] = zero[i][1] = v16i{};
+                store_tile<OutT, true, true>(a, nullptr, stg, zero, m0, br, w, lane);
+            } else {
+                store_zero_rows<OutT>(a, m0, br, w, lane);
+            }
             continue;
         }
         // the first block starts the accumulators from zero (an inline
@@ -361,12 +400,13 @@ __device__ __forceinline__ void consumer(const Args &a, uint4 *lds, const int2 *
         // the buffer of the tile's last block (with its scales) is refilled
         // only after the next barrier, which this wavefront reaches after
         // its reads below
-        store_tile<OutT>(a, buf, stg, acc, m0, br, w, lane);
+        store_tile<OutT, ADDMM, false>(a, buf, stg, acc, m0, br, w, lane);
     }
 }
 
-template <bool OUT_I32>
-__global__ __launch_bounds__(kThreads) void bsr_gemm_kernel(Args a, int slabs) {
+// Two workgroups per CU: four wavefronts per SIMD, at most 128 registers each.
+template <bool OUT_I32, bool ADDMM>
+__global__ __launch_bounds__(kThreads, 4) void bsr_gemm_kernel(Args a, int slabs) {
     using OutT = typename std::conditional<OUT_I32, int32_t, __bf16>::type;
     __shared__ uint4 lds[kLdsSlots];
     __shared__ int2 meta[kSegTiles];  // stored-block range of each tile of the segment
@@ -387,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void bsr_gemm_kernel(Args a, int slabs) {
             const int cnt = min(kSegTiles, nt - s0);
             lds_barrier();
             lds_barrier();
-            consumer<OutT>(a, lds, meta, L, s0, cnt, wave, lane);
+            consumer<OutT, ADDMM>(a, lds, meta, L, s0, cnt, wave, lane);
         }
     } else {
         for (int s0 = 0; s0 < nt; s0 += kSegTiles) {
@@ -412,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void bsr_gemm_kernel(Args a, int slabs) {
 
 hipError_t launch_bsr_gemm(const int8_t *xq, const float *xs, int M, int K, const int32_t *crow,
                            const int32_t *col, const int8_t *values, int nnzb, const float *ws,
-                           int N, void *out, bool out_i32, hipStream_t stream) {
+                           int N, void *out, bool out_i32, hipStream_t stream, const Addmm *am) {
     const int slabs = (M + kBM - 1) / kBM, block_rows = N / kBS;
     const int tiles = slabs * block_rows;
     // two resident workgroups per CU, a multiple of the XCD count
@@ -426,12 +466,15 @@ hipError_t launch_bsr_gemm(const int8_t *xq, const float *xs, int M, int K, cons
         while (per > 1 && std::gcd(per, block_rows) != 1) --per;
         P = per * kXcds;
     }
-    const Args a{xq, xs, crow, col, values, ws, out, nnzb, M, N, K, block_rows};
+    const Args a{xq, xs, crow, col, values, ws, out, nnzb, M, N, K, block_rows,
+                 am ? *am : Addmm{nullptr, 1.0f, 0.0f}};
     const dim3 grid((unsigned)P), block(kThreads);
     if (out_i32)
-        bsr_gemm_kernel<true><<<grid, block, 0, stream>>>(a, slabs);
+        bsr_gemm_kernel<true, false><<<grid, block, 0, stream>>>(a, slabs);
+    else if (am)
+        bsr_gemm_kernel<false, true><<<grid, block, 0, stream>>>(a, slabs);
     else
-        bsr_gemm_kernel<false><<<grid, block, 0, stream>>>(a, slabs);
+        bsr_gemm_kernel<false, false><<<grid, block, 0, stream>>>(a, slabs);
     return hipGetLastError();
 }
 

@@ -37,9 +37,11 @@ hipError_t launch_sparse24_gemm(const int8_t *xq, const float *xs, int M, const 
 // Compute units of the current device (queried once per device).
 int device_cu_count();
 
+// Block-sparse GEMM; am (bf16 output only) selects the addmm epilogue.
 hipError_t launch_bsr_gemm(const int8_t *xq, const float *xs, int M, int K, const int32_t *crow,
                            const int32_t *col, const int8_t *values, int nnzb, const float *ws,
-                           int N, void *out, bool out_i32, hipStream_t stream);
+                           int N, void *out, bool out_i32, hipStream_t stream,
+                           const Addmm *am = nullptr);
 
 }  // namespace w8a8
 

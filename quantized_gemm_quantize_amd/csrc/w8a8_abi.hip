@@ -161,6 +161,32 @@ w8a8_status w8a8_bsr_gemm(const int8_t *xq, const float *x_scale, int64_t M, int
                                             static_cast<hipStream_t>(stream)));
 }
 
+w8a8_status w8a8_bsr_gemm_addmm(const int8_t *xq, const float *x_scale, int64_t M, int64_t K,
+                                const int32_t *crow, const int32_t *col, const int8_t *values,
+                                int64_t nnzb, int64_t bs, const float *w_scale, int64_t N,
+                                const float *bias, float alpha, float beta, void *out,
+                                void *stream) {
+    if (bs != 64) return W8A8_ERR_BLOCKSIZE;
+    if (M < 0 || N <= 0 || N % bs != 0 || K % bs != 0 || nnzb < 0 || too_big(M, N))
+        return W8A8_ERR_SHAPE;
+    if (w8a8_status s = check_k(K)) return s;
+    if (nnzb > (N / bs) * (K / bs)) return W8A8_ERR_SHAPE;
+    if (!std::isfinite(alpha) || !std::isfinite(beta)) return W8A8_ERR_VALUE;
+    if ((M + 127) / 128 > INT_MAX / (N / bs)) return W8A8_ERR_SHAPE;  // grid.x
+    if (M == 0) return W8A8_OK;
+    if (!xq || !x_scale || !crow || !w_scale || !out) return W8A8_ERR_NULL;
+    if (nnzb > 0 && (!col || !values)) return W8A8_ERR_NULL;
+    if (!bias && beta != 0.0f) return W8A8_ERR_NULL;
+    if (misaligned(xq) || misaligned(x_scale) || misaligned(crow) || misaligned(w_scale) ||
+        misaligned(out) || (nnzb > 0 && (misaligned(col) || misaligned(values))) ||
+        (bias && misaligned(bias)))
+        return W8A8_ERR_ALIGN;
+    const w8a8::Addmm am{bias, alpha, beta};
+    return hip_status(w8a8::launch_bsr_gemm(xq, x_scale, (int)M, (int)K, crow, col, values,
+                                            (int)nnzb, w_scale, (int)N, out, false,
+                                            static_cast<hipStream_t>(stream), &am));
+}
+
 w8a8_status w8a8_compress24(const int8_t *wq, int64_t N, int64_t K, int8_t *values,
                             uint32_t *meta, void *stream) {
     if (N < 0 || K <= 0 || K % 128 != 0 || N > INT_MAX / 2 || K > INT_MAX / 2) return W8A8_ERR_SHAPE;

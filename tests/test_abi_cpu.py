@@ -33,8 +33,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_gemm_addmm",
-               "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_compress24", "w8a8_sparse24_gemm",
-               "w4a16_dequant", "w4a16_gemm", "w8a8_status_string", "w8a8_last_hip_error"):
+               "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_bsr_gemm_addmm", "w8a8_compress24",
+               "w8a8_sparse24_gemm", "w4a16_dequant", "w4a16_gemm", "w8a8_status_string",
+               "w8a8_last_hip_error"):
         assert fn in names
 
 
@@ -208,4 +209,27 @@ def test_bsr_validation(lib):
     for k in ("xq", "xs", "crow", "col", "vals", "ws", "out"):
         assert b(*args(**{k: 0})) == NULL, k
         assert b(*args(**{k: P + 2})) == ALIGN, k
+    assert b(*args(M=0, xq=0, xs=0, out=0)) == OK
+
+
+def test_bsr_addmm_validation(lib):
+    b = lib.w8a8_bsr_gemm_addmm
+    args = lambda **kw: [kw.get("xq", P), kw.get("xs", P), kw.get("M", 32), kw.get("K", 128),
+                         kw.get("crow", P), kw.get("col", P), kw.get("vals", P),
+                         kw.get("nnzb", 2), kw.get("bs", 64), kw.get("ws", P), kw.get("N", 128),
+                         kw.get("bias", P), kw.get("alpha", 1.0), kw.get("beta", 1.0),
+                         kw.get("out", P), None]
+    assert b(*args(bs=32)) == BLK
+    assert b(*args(N=96)) == SHAPE                      # N % 64
+    assert b(*args(K=80)) == SHAPE                      # K % 64
+    assert b(*args(M=-1)) == SHAPE
+    assert b(*args(nnzb=-1)) == SHAPE
+    assert b(*args(nnzb=5)) == SHAPE
+    assert b(*args(K=133184)) == KOVF
+    assert b(*args(alpha=float("inf"))) == VALUE
+    assert b(*args(beta=float("nan"))) == VALUE
+    for k in ("xq", "xs", "crow", "col", "vals", "ws", "out", "bias"):
+        assert b(*args(**{k: 0})) == NULL, k
+        assert b(*args(**{k: P + 2})) == ALIGN, k
+    assert b(*args(bias=0, beta=0.0, M=0)) == OK        # no bias term, empty: no launch
     assert b(*args(M=0, xq=0, xs=0, out=0)) == OK

@@ -265,6 +265,21 @@ def _bf16_ulp(x: np.ndarray) -> np.ndarray:
     return np.exp2(np.floor(np.log2(a)) - 7)
 
 
+def _assert_addmm_close(oracle, got, acc, sx, sw, bias, alpha, beta):
+    """got (bf16 bits) against the oracle's float64 addmm definition: within one bf16 ulp plus
+    2^-20 of |alpha * acc * sx * sw| + |beta * bias| (the fp32 rounding of the two terms)."""
+    ref = oracle.epilogue_addmm_bf16(acc, sx, sw, bias, alpha, beta)
+    g = bf16_bits_to_f32(got).astype(np.float64)
+    o = bf16_bits_to_f32(ref).astype(np.float64)
+    t = acc.astype(np.float64) * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]
+    mag = np.abs(alpha * t)
+    if bias is not None:
+        mag = mag + np.abs(beta * bias.astype(np.float64))[None, :]
+    bound = _bf16_ulp(np.maximum(np.abs(g), np.abs(o))) + mag * 2.0 ** -20
+    worst = np.max(np.abs(g - o) - bound)
+    assert (np.abs(g - o) <= bound).all(), worst
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (16, 256, 512), (64, 128, 256), (300, 512, 320),
                                    (129, 1024, 4096)])
 @pytest.mark.parametrize("alpha,beta,with_bias", [(1.0, 1.0, True), (0.5, -2.0, True),
@@ -281,16 +296,7 @@ def test_gemm_addmm(b, oracle, M, N, K, alpha, beta, with_bias):
     bias_dev = torch.from_numpy(bias).to(DEV) if with_bias else None
     got = bf16_bits(b.w8a8_gemm_addmm(xq, sx, wq, sw, bias=bias_dev, alpha=alpha, beta=beta))
     acc = oracle.gemm_i32(xq_ref, wq_ref)
-    ref = oracle.epilogue_addmm_bf16(acc, sx_ref, sw_ref, bias, alpha, beta)
-    g = bf16_bits_to_f32(got).astype(np.float64)
-    o = bf16_bits_to_f32(ref).astype(np.float64)
-    t = acc.astype(np.float64) * sx_ref.astype(np.float64)[:, None] * sw_ref.astype(np.float64)[None, :]
-    mag = np.abs(alpha * t)
-    if with_bias:
-        mag = mag + np.abs(beta * bias.astype(np.float64))[None, :]
-    bound = _bf16_ulp(np.maximum(np.abs(g), np.abs(o))) + mag * 2.0 ** -20
-    worst = np.max(np.abs(g - o) - bound)
-    assert (np.abs(g - o) <= bound).all(), worst
+    _assert_addmm_close(oracle, got, acc, sx_ref, sw_ref, bias, alpha, beta)
     if alpha == 1.0 and not with_bias:
         assert np.array_equal(got, bf16_bits(b.w8a8_gemm(xq, sx, wq, sw)))
 
@@ -600,6 +606,50 @@ def test_bsr_workload_full_size(b, oracle, name):
     worst, n_empty = _bsr_case(b, oracle, cfg["M"], cfg["N"], cfg["K"], cfg["zero_frac"], seed=0,
                                rows=inp_rows)
     log(f"  bsr: {len(inp_rows)} rows compared, max {worst} ulp, {n_empty} empty block rows")
+
+
+def _bsr_addmm_case(b, oracle, M, N, K, zero_frac, seed, alpha, beta, with_bias, rows=None):
+    inp = make_linear(M, N, K, seed=seed, bs=64, zero_frac=zero_frac)
+    xq, sx, xq_ref, sx_ref = _check_quantize(b, oracle, inp.x_bits, "bsr addmm X")
+    wq, sw, wq_ref, sw_ref = gpu_weights(b, oracle, inp.w)
+    crow, col, values = bsr_from_dense(wq_ref, inp.block_mask, 64)
+    if values.shape[0] == 0:
+        values = np.zeros((0, 64, 64), np.int8)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    rng = np.random.default_rng(seed + 11)
+    bias = (rng.standard_normal(N) * 0.5).astype(np.float32) if with_bias else None
+    got = bf16_bits(b.w8a8_bsr_gemm_addmm(xq, sx, t(crow), t(col), t(values), sw,
+                                          bias=None if bias is None else t(bias),
+                                          alpha=alpha, beta=beta))
+    rows = np.arange(M) if rows is None else rows
+    acc_ref = oracle.bsr_gemm_i32(xq_ref[rows], crow, col, values, N)
+    _assert_addmm_close(oracle, got[rows], acc_ref, sx_ref[rows], sw_ref, bias, alpha, beta)
+    if alpha == 1.0 and not with_bias:
+        plain = bf16_bits(b.w8a8_bsr_gemm(xq, sx, t(crow), t(col), t(values), sw))
+        assert np.array_equal(got, plain)
+    return int((np.diff(crow) == 0).sum())
+
+
+@pytest.mark.parametrize("M,N,K,zf", [(16, 128, 128, 0.5), (129, 256, 192, 0.7),
+                                      (300, 512, 320, 0.9), (200, 192, 128, 1.0),
+                                      (64, 320, 256, 0.0)])
+@pytest.mark.parametrize("alpha,beta,with_bias", [(1.0, 1.0, True), (0.5, -2.0, True),
+                                                  (-1.25, 0.0, True), (2.0, 0.0, False),
+                                                  (1.0, 0.0, False)])
+def test_bsr_addmm(b, oracle, M, N, K, zf, alpha, beta, with_bias):
+    """BSR addmm epilogue against the oracle's float64 definition, including block rows without
+    stored blocks (bf16(beta * bias[n])); alpha = 1 without a bias is the plain BSR output."""
+    log(f"bsr addmm M={M} N={N} K={K} zero_frac={zf} alpha={alpha} beta={beta} bias={with_bias}")
+    _bsr_addmm_case(b, oracle, M, N, K, zf, M + N + K + 3, alpha, beta, with_bias)
+
+
+def test_bsr_addmm_workload_full_size(b, oracle):
+    cfg = CONFIGS["bsr"]
+    log(f"bsr addmm workload {cfg}")
+    rows = _sampled_rows(cfg["M"])
+    n_empty = _bsr_addmm_case(b, oracle, cfg["M"], cfg["N"], cfg["K"], cfg["zero_frac"], 0,
+                              0.75, 1.5, True, rows=rows)
+    log(f"  bsr addmm: {len(rows)} rows compared, {n_empty} empty block rows")
 
 
 def test_bsr_many_tiles_per_workgroup(b, oracle):
