@@ -32,7 +32,10 @@ __device__ __forceinline__ float bf16_to_float(uint16_t bits) {
 
 // 8 codes (code e in bits 4e .. 4e+3) -> 8 bf16 weights, packed 2 per word.
 __device__ __forceinline__ uint4 dequant8(uint32_t packed, float s, float z) {
-    const uint32_t even = packed & 0x0F0F0F0Fu, odd = (packed >> 4) & 0x0F0F0F0Fu;
+    uint32_t even = packed & 0x0F0F0F0Fu, odd = (packed >> 4) & 0x0F0F0F0Fu;
+    // opaque to the optimizer: each code then converts with one
+    // v_cvt_f32_ubyteN instead of a bit-field extract and a conversion
+    asm volatile("" : "+v"(even), "+v"(odd));
     float d[8];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -177,8 +180,9 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
     constexpr int XBUF = 4, WBUF = 2;
     constexpr int XLD = XS / 256;                              // activation loads per wavefront
     constexpr int CODES = BN * 64 / 256;                       // weight codes per thread per stage
-    constexpr int NLD = XLD + 3;                               // + codes, scale, zero
-    static_assert(CODES == 32 || CODES == 16, "16 or 8 bytes of codes per thread");
+    constexpr int CLD = CODES == 64 ? 2 : 1;                   // 16-byte code loads (or one 8-byte)
+    constexpr int NLD = XLD + CLD + 2;                         // + codes, scale, zero
+    static_assert(CODES == 64 || CODES == 32 || CODES == 16, "32, 16 or 8 bytes of codes per thread");
     static_assert(WM * WN * 2 * 4 <= (XBUF * XS + WBUF * WS) * 16, "bf16 tile fits in LDS");
     static_assert(TM >= 1 && TN >= 1 && 2 * NLD < 64, "wavefront tiles and the vmcnt range");
     __shared__ uint4 lds[XBUF * XS + WBUF * WS];
@@ -216,7 +220,12 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
     };
     auto load_codes = [&](int j, Codes &c) {
         const uint8_t *src = wsrc + 32 * j;
-        if constexpr (CODES == 32) {
+        if constexpr (CODES == 64) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(src);
+            const uint4 u = *reinterpret_cast<const uint4 *>(src + 16);
+            c.c[0] = v.x; c.c[1] = v.y; c.c[2] = v.z; c.c[3] = v.w;
+            c.c[4] = u.x; c.c[5] = u.y; c.c[6] = u.z; c.c[7] = u.w;
+        } else if constexpr (CODES == 32) {
             const uint4 v = *reinterpret_cast<const uint4 *>(src);
             c.c[0] = v.x; c.c[1] = v.y; c.c[2] = v.z; c.c[3] = v.w;
         } else {
@@ -267,7 +276,12 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
 #pragma unroll
                 for (int q = 0; q < TN; ++q)
                     acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[q], xa[i], acc[i][q], 0, 0, 0);
-            if (u < CODES / 8) store_word(next, u, nb);
+            // this step's share of the code words (one or two; none in the
+            // last steps when there are only two)
+            constexpr int WPS = CODES / 8 > 4 ? CODES / 32 : 1;
+#pragma unroll
+            for (int i = 0; i < WPS; ++i)
+                if (u * WPS + i < CODES / 8) store_word(next, u * WPS + i, nb);
         }
     };
 
@@ -392,11 +406,12 @@ hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *wq4, const uint1
         default: break;
     }
     // 256 x 64 tiles (4 wavefronts along M: half the dequantization per output
-    // of 128 x 128) when they fill the chip, 128 x 128 next, else 64 x 64
+    // of 128 x 128, measured faster at M = 1024) when they fill the chip, then
+    // 128 x 64 (also 4 wavefronts along M), else 64 x 64
     const long t256 = (long)((M + 255) / 256) * ((N + 63) / 64);
-    const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
+    const long t128 = (long)((M + 127) / 128) * ((N + 63) / 64);
     if (t256 >= 256) return launch_tiled<256, 64, 4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-    if (t128 >= 256) return launch_tiled<128, 128, 2>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    if (t128 >= 256) return launch_tiled<128, 64, 4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
     return launch_tiled<64, 64, 2>(x, M, wq4, scales, zeros, N, K, G, out, stream);
 }
 

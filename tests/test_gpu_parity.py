@@ -549,8 +549,9 @@ def _w4a16_case(b, oracle, inp, what, rows=None):
     # weight-streaming path (M <= 64)
     (1, 16, 128, 128), (5, 48, 256, 32), (16, 128, 4096, 128), (17, 64, 640, 64),
     (33, 32, 1024, 256), (64, 96, 512, 128),
-    # tiled path: 64 x 64 tiles (ragged M and N), 128 x 128 and 256 x 64 tiles (256+ of them)
+    # tiled path: 64 x 64 tiles (ragged M and N), 128 x 64 and 256 x 64 tiles (256+ of them)
     (65, 64, 128, 128), (100, 80, 384, 32), (130, 272, 1024, 64), (257, 528, 256, 128),
+    (400, 4160, 256, 64), (300, 8192, 128, 32),
     (2048, 2048, 256, 128), (1100, 4096, 128, 128), (1024, 4112, 256, 64), (512, 8192, 384, 128),
 ])
 def test_w4a16_gemm_shapes(b, oracle, M, N, K, G):
