@@ -54,6 +54,21 @@ __global__ __launch_bounds__(KSPLIT *kWave) void gemm_decode_kernel(
 #pragma unroll
     for (int mb = 0; mb < MT; ++mb) acc[mb] = v4i{};
 
+    // the epilogue's scales (and bias) for this thread's outputs, loaded
+    // before the weights: they land with them instead of costing one more
+    // memory round trip after the reduction
+    constexpr int kThreadsWg = KSPLIT * kWave;
+    constexpr int EPT = (MT * 256 + kThreadsWg - 1) / kThreadsWg;  // outputs per thread
+    float esx[EPT], esw[EPT], ebias[EPT];
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int e = min((int)threadIdx.x + q * kThreadsWg, MT * 256 - 1);
+        const int m = min((e >> 8) * 16 + ((e >> 4) & 15), M - 1), n = n0 + (e & 15);
+        esx[q] = OUT_I32 ? 0.0f : sa[m];
+        esw[q] = OUT_I32 ? 0.0f : sb[n];
+        ebias[q] = ADDMM && am.bias ? am.bias[n] : 0.0f;
+    }
+
     const int total_steps = (K + 63) / 64;
     const int s_begin = wave * steps_per_wave;
     const int s_end = min(s_begin + steps_per_wave, total_steps);
@@ -82,7 +97,10 @@ __global__ __launch_bounds__(KSPLIT *kWave) void gemm_decode_kernel(
 
     // one output element per thread: row i, column j of 16x16 tile mb sits in
     // lane j + 16 * (i / 4), element i % 4
-    for (int e = threadIdx.x; e < MT * 256; e += KSPLIT * kWave) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int e = (int)threadIdx.x + q * kThreadsWg;
+        if (e >= MT * 256) continue;
         const int mb = e >> 8, i = (e >> 4) & 15, j = e & 15;
         const int m = mb * 16 + i;
         if (m >= M) continue;
@@ -94,8 +112,7 @@ __global__ __launch_bounds__(KSPLIT *kWave) void gemm_decode_kernel(
         if constexpr (OUT_I32) {
             static_cast<int32_t *>(out)[(int64_t)m * N + n] = sum;
         } else {
-            const float v =
-                addmm<ADDMM>((float)sum * sa[m] * sb[n], am, ADDMM && am.bias ? am.bias[n] : 0.0f);
+            const float v = addmm<ADDMM>((float)sum * esx[q] * esw[q], am, ebias[q]);
             static_cast<__bf16 *>(out)[(int64_t)m * N + n] = (__bf16)v;
         }
     }
