@@ -115,11 +115,14 @@ hipError_t launch_wpr(const T *x, int64_t M, int K, int8_t *xq, float *xs, hipSt
 }
 
 // Four wavefronts per row while that still leaves at least 8192 wavefronts
-// and each lane 2+ chunks; otherwise one wavefront per row.
+// and each lane 2+ chunks; otherwise the fewest wavefronts per row (1, 2 or
+// 4) that hold the row in registers, so it is read once.
 template <typename T>
 hipError_t launch_quantize(const T *x, int64_t M, int K, int8_t *xq, float *xs, hipStream_t stream) {
     if (M < 8192 && K >= 4 * kWave * 8 * 2) return launch_wpr<T, 4>(x, M, K, xq, xs, stream);
-    return launch_wpr<T, 1>(x, M, K, xq, xs, stream);
+    if (K <= kWave * 8 * kMaxRegChunks) return launch_wpr<T, 1>(x, M, K, xq, xs, stream);
+    if (K <= 2 * kWave * 8 * kMaxRegChunks) return launch_wpr<T, 2>(x, M, K, xq, xs, stream);
+    return launch_wpr<T, 4>(x, M, K, xq, xs, stream);
 }
 
 }  // namespace

@@ -79,7 +79,9 @@ def _check_quantize(b, oracle, x_bits, what):
 
 
 @pytest.mark.parametrize("M,K", [(1, 16), (3, 48), (5, 256), (7, 512), (9, 528), (4, 4096),
-                                 (6, 4112), (3, 8192), (2, 16400), (130, 1024)])
+                                 (6, 4112), (3, 8192), (2, 16400), (130, 1024),
+                                 # many rows: one, two or four wavefronts per row by K
+                                 (8200, 4096), (8192, 4112), (8200, 6160), (8256, 8208)])
 def test_quantize_rows_shapes(b, oracle, M, K):
     log(f"quantize_rows M={M} K={K}")
     inp = make_linear(M, 16, K, seed=M * 7 + K)
@@ -116,7 +118,7 @@ def test_quantize_rows_special_rows(b, oracle):
     _check_quantize(b, oracle, f32_to_bf16_bits(fam), "near-tie family")
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "prefill_outliers", "large_m", "bsr"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill_outliers", "large_m", "bsr", "bsr_fc2"])
 def test_quantize_rows_workloads(b, oracle, name):
     log(f"quantize_rows workload {name} {CONFIGS[name]}")
     inp = make_inputs(name)
