@@ -81,7 +81,7 @@ typedef enum {
  *           xq = 0 for an all-zero row. Division is IEEE binary32, rounding
  *           half to even, subnormals kept. Non-finite inputs are outside the
  *           domain (output unspecified).
- * Errors: NULL, SHAPE (M < 0, K <= 0, K % 16), K_OVERFLOW, ALIGN, HIP.
+ * Errors: NULL, SHAPE (M < 0, M > 2^31 - 1, K <= 0, K % 16), K_OVERFLOW, ALIGN, HIP.
  */
 w8a8_status w8a8_quantize_rows(const void *x_bf16, int64_t M, int64_t K, int8_t *xq,
                                float *x_scale, void *stream);

@@ -45,7 +45,7 @@ w8a8_status quantize_entry(const T *x, int64_t M, int64_t K, int8_t *xq, float *
     if (M < 0) return W8A8_ERR_SHAPE;
     if (w8a8_status s = check_k(K)) return s;
     if (M == 0) return W8A8_OK;
-    if (M > (int64_t)INT_MAX * 4) return W8A8_ERR_SHAPE;  // grid.x limit, 4 rows per block
+    if (M > INT_MAX) return W8A8_ERR_SHAPE;  // grid.x: at least one row per workgroup
     if (!x || !xq || !x_scale) return W8A8_ERR_NULL;
     if (misaligned(x) || misaligned(xq) || misaligned(x_scale)) return W8A8_ERR_ALIGN;
     return hip_status(launch(x, M, (int)K, xq, x_scale, static_cast<hipStream_t>(stream)));

@@ -69,6 +69,7 @@ def test_quantize_validation(lib, fn):
     assert f(P, 4, 0, P, P, None) == SHAPE
     assert f(P, 4, 24, P, P, None) == SHAPE          # K % 16
     assert f(P, 4, 133152, P, P, None) == KOVF
+    assert f(P, 2 ** 31, 64, P, P, None) == SHAPE     # more rows than workgroups can be launched
     assert f(0, 4, 64, P, P, None) == NULL
     assert f(P, 4, 64, 0, P, None) == NULL
     assert f(P, 4, 64, P, 0, None) == NULL
