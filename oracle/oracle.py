@@ -59,7 +59,7 @@ def load_oracle():
     lib.oracle_compress24.restype = None
     lib.oracle_decompress24.argtypes = [p, p, i64, i64, p]
     lib.oracle_decompress24.restype = ctypes.c_int
-    lib.oracle_w4a16_dequant.argtypes = [p, p, p, i64, i64, i64, p]
+    lib.oracle_w4a16_dequant.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int, p]
     lib.oracle_w4a16_dequant.restype = None
     lib.oracle_bf16_gemm.argtypes = [p, p, i64, i64, i64, p]
     lib.oracle_bf16_gemm.restype = None
@@ -201,9 +201,11 @@ def decompress24(values: np.ndarray, meta: np.ndarray) -> np.ndarray:
     return w
 
 
-def w4a16_dequant(wq4: np.ndarray, scales: np.ndarray, zeros: np.ndarray) -> np.ndarray:
-    """Packed u4 [N,K/2] + bf16 scales/zeros [N,K/G] (bit patterns) -> bf16 w [N,K] (bits):
-    w = bf16(bf16(q - z) * s)."""
+def w4a16_dequant(wq4: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+                  signed: bool = False) -> np.ndarray:
+    """Packed 4-bit codes [N,K/2] + bf16 scales/zeros [N,K/G] (bit patterns) -> bf16 w [N,K]
+    (bits): w = bf16(bf16(q - z) * s), q the nibble (u4, 0..15) or its 4-bit two's
+    complement (s4, -8..7)."""
     wq4 = _c(wq4, np.uint8)
     scales = _c(scales, np.uint16)
     zeros = _c(zeros, np.uint16)
@@ -213,7 +215,8 @@ def w4a16_dequant(wq4: np.ndarray, scales: np.ndarray, zeros: np.ndarray) -> np.
         raise ValueError("W4A16 shapes")
     G = K // scales.shape[1]
     w = np.empty((N, K), np.uint16)
-    load_oracle().oracle_w4a16_dequant(_ptr(wq4), _ptr(scales), _ptr(zeros), N, K, G, _ptr(w))
+    load_oracle().oracle_w4a16_dequant(_ptr(wq4), _ptr(scales), _ptr(zeros), N, K, G,
+                                       1 if signed else 0, _ptr(w))
     return w
 
 

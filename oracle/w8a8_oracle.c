@@ -309,20 +309,25 @@ int oracle_decompress24(const int8_t *values, const uint32_t *meta, int64_t N, i
 static double bf16_to_f64(uint16_t bits) { return (double)bf16_bits_to_float(bits); }
 
 /*
- * W4A16 dequantization. wq4 [N, K/2] bytes: byte j of row n holds q[n][2j] in
- * its low nibble and q[n][2j+1] in its high nibble (u4, 0..15). scales, zeros:
- * bf16 [N, K/G]. w [N,K] bf16 (bit patterns):
+ * W4A16 dequantization. wq4 [N, K/2] bytes: byte j of row n holds code
+ * c[n][2j] in its low nibble and c[n][2j+1] in its high nibble; q = c (u4,
+ * 0..15) or, with signed_codes, the 4-bit two's complement of c (s4, -8..7).
+ * scales, zeros: bf16 [N, K/G]. w [N,K] bf16 (bit patterns):
  *   w[n][k] = bf16(bf16(q - z) * s),  s = scales[n][k/G], z = zeros[n][k/G].
- * q - z and (q - z) * s are exact in float64 (at most 8 + 8 significant bits),
- * so each bf16() is one rounding of the exact value.
+ * q - z is exact in float64 unless q != 0 and |z| < 2^-41, where its float64
+ * rounding moves it by far less than a bf16 ulp and never onto a bf16 tie, and
+ * the product of two bf16 values is exact, so each bf16() here rounds the
+ * exact value once.
  */
 void oracle_w4a16_dequant(const uint8_t *wq4, const uint16_t *scales, const uint16_t *zeros,
-                          int64_t N, int64_t K, int64_t G, uint16_t *w) {
+                          int64_t N, int64_t K, int64_t G, int signed_codes, uint16_t *w) {
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t k = 0; k < K; ++k) {
             const uint8_t byte = wq4[n * (K / 2) + k / 2];
-            const int q = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+            const int nibble = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+            /* u4: q = nibble in [0, 15]; s4: the nibble's 4-bit two's complement in [-8, 7] */
+            const int q = signed_codes && nibble >= 8 ? nibble - 16 : nibble;
             const double s = bf16_to_f64(scales[n * (K / G) + k / G]);
             const double z = bf16_to_f64(zeros[n * (K / G) + k / G]);
             const double shifted = bf16_to_f64(oracle_bf16_rne_from_f64((double)q - z));

@@ -436,15 +436,46 @@ def test_w4a16_dequant_hand_worked(oracle):
         assert float(bf16_bits_to_f32(w)[0, 0]) == c["w"]
 
 
-def test_w4a16_dequant_matches_exact_rationals(oracle):
+def test_w4a16_dequant_signed_hand_worked(oracle):
+    """Signed 4-bit codes (s4): the worked cases of the fixture."""
+    g = _load("w4a16_worked.json")
+    c = g["nibbles_s4"]
+    w = oracle.w4a16_dequant(np.array([c["bytes"]], np.uint8), _bits(c["scale_bits"])[None, :],
+                             _bits(c["zero_bits"])[None, :], signed=True)
+    assert bf16_bits_to_f32(w)[0].tolist() == c["w"]
+    c = g["s4_shift_rounding"]
+    wq4 = np.array([[c["q"] | (c["q"] << 4)]], np.uint8)
+    w = oracle.w4a16_dequant(wq4, _bits(c["scale_bits"])[None, :], _bits(c["zero_bits"])[None, :],
+                             signed=True)
+    assert w[0].tolist() == [int(c["w_bits"], 16)] * 2
+    assert float(bf16_bits_to_f32(w)[0, 0]) == c["w"]
+
+
+def test_w4a16_dequant_signed_agrees_below_eight(oracle):
+    """Codes 0..7 mean the same as u4 and s4; codes 8..15 differ (by 16 before the shift)."""
+    from quantized_gemm_quantize_amd.inputs import make_w4a16
+    inp = make_w4a16(1, 4, 256, G=64, seed=13)
+    wu = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros)
+    ws = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros, signed=True)
+    q = np.empty((4, 256), np.int64)
+    q[:, 0::2] = inp.wq4 & 15
+    q[:, 1::2] = inp.wq4 >> 4
+    assert np.array_equal(wu[q < 8], ws[q < 8])
+    assert not np.array_equal(wu[q >= 8], ws[q >= 8])
+
+
+@pytest.mark.parametrize("signed", [False, True])
+def test_w4a16_dequant_matches_exact_rationals(oracle, signed):
     """Every dequantized weight of a random layer against bf16(bf16(q - z) * s) evaluated on
-    exact rationals with bf16 rounding written out (the exact module)."""
+    exact rationals with bf16 rounding written out (the exact module), for u4 and s4 codes."""
     from quantized_gemm_quantize_amd.inputs import make_w4a16
     inp = make_w4a16(1, 6, 256, G=128, seed=9)
-    w = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros)
+    w = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros, signed=signed)
     q = np.empty((6, 256), np.int64)
     q[:, 0::2] = inp.wq4 & 15
     q[:, 1::2] = inp.wq4 >> 4
+    if signed:
+        q = np.where(q >= 8, q - 16, q)
     s = bf16_bits_to_f32(inp.scales)
     z = bf16_bits_to_f32(inp.zeros)
     for n in range(6):
