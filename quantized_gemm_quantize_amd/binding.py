@@ -62,8 +62,8 @@ def load():
     lib.w8a8_fused_linear.argtypes = [p, i64, i64, p, p, i64, p, f32, f32, p, p]
     lib.w8a8_compress24.argtypes = [p, i64, i64, p, p, p]
     lib.w8a8_sparse24_gemm.argtypes = [p, p, i64, p, p, p, i64, i64, p, i32, p]
-    lib.w4a16_dequant.argtypes = [p, p, p, i64, i64, i64, p, p]
-    lib.w4a16_gemm.argtypes = [p, i64, p, p, p, i64, i64, i64, p, p]
+    lib.w4a16_dequant.argtypes = [p, p, p, i64, i64, i64, i32, p, p]
+    lib.w4a16_gemm.argtypes = [p, i64, p, p, p, i64, i64, i64, i32, p, p]
     for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_gemm_addmm",
                "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_bsr_gemm_addmm", "w8a8_compress24",
                "w8a8_sparse24_gemm",
@@ -234,8 +234,12 @@ def _w4a16_operands(wq4, scales, zeros):
     return N, K, K // scales.shape[1]
 
 
-def w4a16_dequant(wq4, scales, zeros, out=None, stream=None):
-    """Packed u4 [N,K/2] + bf16 scales/zeros [N,K/G] -> bf16 w [N,K] = bf16(bf16(q - z) * s)."""
+W4A16_CODES_U4, W4A16_CODES_S4 = 0, 1
+
+
+def w4a16_dequant(wq4, scales, zeros, signed=False, out=None, stream=None):
+    """Packed 4-bit codes [N,K/2] + bf16 scales/zeros [N,K/G] -> bf16 w [N,K] =
+    bf16(bf16(q - z) * s); q the code (u4) or, with signed, its 4-bit two's complement (s4)."""
     N, K, G = _w4a16_operands(wq4, scales, zeros)
     if out is None:
         out = torch.empty((N, K), dtype=torch.bfloat16, device=wq4.device)
@@ -243,12 +247,13 @@ def w4a16_dequant(wq4, scales, zeros, out=None, stream=None):
     if tuple(out.shape) != (N, K):
         raise ValueError("out shape")
     _call("w4a16_dequant", wq4.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K, G,
-          out.data_ptr(), _stream_handle(stream))
+          W4A16_CODES_S4 if signed else W4A16_CODES_U4, out.data_ptr(), _stream_handle(stream))
     return out
 
 
-def w4a16_gemm(x, wq4, scales, zeros, out=None, stream=None):
-    """out [M,N] bf16 = x [M,K] bf16 times the dequantized W4 weights, fused."""
+def w4a16_gemm(x, wq4, scales, zeros, signed=False, out=None, stream=None):
+    """out [M,N] bf16 = x [M,K] bf16 times the dequantized 4-bit weights (u4, or s4 with
+    signed), fused."""
     _check_tensor(x, "x", torch.bfloat16, 2)
     N, K, G = _w4a16_operands(wq4, scales, zeros)
     M = x.shape[0]
@@ -256,7 +261,8 @@ def w4a16_gemm(x, wq4, scales, zeros, out=None, stream=None):
         raise ValueError("operand shapes")
     out = _out(out, M, N, _out_dtype("bf16"), x.device)
     _call("w4a16_gemm", x.data_ptr(), M, wq4.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N,
-          K, G, out.data_ptr(), _stream_handle(stream))
+          K, G, W4A16_CODES_S4 if signed else W4A16_CODES_U4, out.data_ptr(),
+          _stream_handle(stream))
     return out
 
 

@@ -6,9 +6,11 @@
 //   w[n,k] = bf16(bf16(q[n,k] - z[n,g]) * s[n,g]),  g = k / G
 //   out[m,n] = bf16(sum_k x[m,k] * w[n,k])           (fp32 accumulation)
 //
-// Packing: byte j of weight row n holds q[n,2j] in its low nibble and
-// q[n,2j+1] in its high nibble (the pages' simple row interleave: no tiling or
-// reordering of the weight). q - z is exact in fp32 (q <= 15, z a bf16), and
+// Packing: byte j of weight row n holds code c[n,2j] in its low nibble and
+// c[n,2j+1] in its high nibble (the pages' simple row interleave: no tiling or
+// reordering of the weight). q = c for unsigned codes (u4, 0..15) and the
+// 4-bit two's complement of c for signed ones (s4, -8..7): the page's kernel
+// takes both. q - z is exact in fp32 (q <= 15, z a bf16), and
 // so is the product of two bf16 values, so each bf16() below is one
 // round-to-nearest-even of the exact value, as in the elementwise bf16
 // arithmetic it stands for, and the dequantized weights are bit-exact.
@@ -31,7 +33,11 @@ __device__ __forceinline__ float bf16_to_float(uint16_t bits) {
 }
 
 // 8 codes (code e in bits 4e .. 4e+3) -> 8 bf16 weights, packed 2 per word.
+// S4: signed codes. c ^ 8 is q + 8 in 0..15, converted like an unsigned code;
+// subtracting 8 is exact, so q - z still takes a single rounding.
+template <bool S4>
 __device__ __forceinline__ uint4 dequant8(uint32_t packed, float s, float z) {
+    if constexpr (S4) packed ^= 0x88888888u;
     uint32_t even = packed & 0x0F0F0F0Fu, odd = (packed >> 4) & 0x0F0F0F0Fu;
     // opaque to the optimizer: each code then converts with one
     // v_cvt_f32_ubyteN instead of a bit-field extract and a conversion
@@ -39,8 +45,13 @@ __device__ __forceinline__ uint4 dequant8(uint32_t packed, float s, float z) {
     float d[8];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        d[2 * b] = (float)((even >> (8 * b)) & 0xFFu) - z;
-        d[2 * b + 1] = (float)((odd >> (8 * b)) & 0xFFu) - z;
+        float qe = (float)((even >> (8 * b)) & 0xFFu), qo = (float)((odd >> (8 * b)) & 0xFFu);
+        if constexpr (S4) {
+            qe -= 8.0f;
+            qo -= 8.0f;
+        }
+        d[2 * b] = qe - z;
+        d[2 * b + 1] = qo - z;
     }
     uint32_t o[4];
 #pragma unroll
@@ -52,6 +63,7 @@ __device__ __forceinline__ uint4 dequant8(uint32_t packed, float s, float z) {
 }
 
 // One thread per 8 weights: w [N,K] bf16.
+template <bool S4>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict__ wq4,
                                                        const uint16_t *__restrict__ scales,
                                                        const uint16_t *__restrict__ zeros,
@@ -63,7 +75,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict
     const int64_t n = k8 / K;
     const int k = (int)(k8 % K);
     const int64_t gi = n * (K / G) + k / G;
-    w[t] = dequant8(wq4[t], bf16_to_float(scales[gi]), bf16_to_float(zeros[gi]));
+    w[t] = dequant8<S4>(wq4[t], bf16_to_float(scales[gi]), bf16_to_float(zeros[gi]));
 }
 
 // Weight-streaming W4A16 GEMM for M <= 64: one workgroup per 16 output
@@ -75,7 +87,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict
 // of 8 columns (the same permutation of K on both operands).
 constexpr int kSplit = 8;
 
-template <int MT>
+template <int MT, bool S4>
 __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_kernel(
     const uint16_t *__restrict__ X, const uint8_t *__restrict__ wq4,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -111,7 +123,7 @@ __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_kernel(
         const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const v8bf a = __builtin_bit_cast(v8bf, dequant8(cw[t], s, z));
+            const v8bf a = __builtin_bit_cast(v8bf, dequant8<S4>(cw[t], s, z));
 #pragma unroll
             for (int mb = 0; mb < MT; ++mb)
                 acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -139,12 +151,12 @@ __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_kernel(
     }
 }
 
-template <int MT>
+template <int MT, bool S4>
 hipError_t launch_decode_mt(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
                             const uint16_t *zeros, int N, int K, int G, uint16_t *out,
                             hipStream_t stream) {
     const int chunks_per_wave = (K / 128 + kSplit - 1) / kSplit;
-    w4a16_decode_kernel<MT><<<dim3((unsigned)(N / 16)), dim3(kSplit * kWave), 0, stream>>>(
+    w4a16_decode_kernel<MT, S4><<<dim3((unsigned)(N / 16)), dim3(kSplit * kWave), 0, stream>>>(
         x, wq4, scales, zeros, out, M, N, K, G, chunks_per_wave);
     return hipGetLastError();
 }
@@ -169,7 +181,7 @@ typedef __attribute__((address_space(1))) void global_void;
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int BM, int BN, int WAVES_M>
+template <int BM, int BN, int WAVES_M, bool S4>
 __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ X, const uint8_t *__restrict__ wq4,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -241,7 +253,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
     // word i of a thread's codes, dequantized into its weight buffer slot
     auto store_word = [&](const Codes &c, int i, uint4 *__restrict__ wb) {
         wb[wr * 8 + ((part * (CODES / 8) + i) ^ swz(wr))] =
-            dequant8(c.c[i], bf16_to_float(c.s), bf16_to_float(c.z));
+            dequant8<S4>(c.c[i], bf16_to_float(c.s), bf16_to_float(c.z));
     };
     auto load_x = [&](int j, uint4 *__restrict__ buf) {
 #pragma unroll
@@ -374,35 +386,35 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
     }
 }
 
-template <int BM, int BN, int WAVES_M>
+template <int BM, int BN, int WAVES_M, bool S4>
 hipError_t launch_tiled(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
                         const uint16_t *zeros, int N, int K, int G, uint16_t *out,
                         hipStream_t stream) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    w4a16_tiled_kernel<BM, BN, WAVES_M><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream>>>(
+    w4a16_tiled_kernel<BM, BN, WAVES_M, S4><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream>>>(
         x, wq4, scales, zeros, out, M, N, K, G, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_dequant(const uint8_t *wq4, const uint16_t *scales, const uint16_t *zeros, int N,
-                          int K, int G, uint16_t *w, hipStream_t stream) {
+template <bool S4>
+hipError_t launch_dequant_codes(const uint8_t *wq4, const uint16_t *scales, const uint16_t *zeros,
+                                int N, int K, int G, uint16_t *w, hipStream_t stream) {
     const int64_t words = (int64_t)N * K / 8;
-    dequant_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream>>>(
+    dequant_kernel<S4><<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream>>>(
         reinterpret_cast<const uint32_t *>(wq4), scales, zeros, words, K, G,
         reinterpret_cast<uint4 *>(w));
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
-                       const uint16_t *zeros, int N, int K, int G, uint16_t *out,
-                       hipStream_t stream) {
+template <bool S4>
+hipError_t launch_gemm_codes(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
+                             const uint16_t *zeros, int N, int K, int G, uint16_t *out,
+                             hipStream_t stream) {
     switch ((M + 15) / 16) {
-        case 1: return launch_decode_mt<1>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-        case 2: return launch_decode_mt<2>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-        case 3: return launch_decode_mt<3>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-        case 4: return launch_decode_mt<4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+        case 1: return launch_decode_mt<1, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+        case 2: return launch_decode_mt<2, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+        case 3: return launch_decode_mt<3, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+        case 4: return launch_decode_mt<4, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
         default: break;
     }
     // 256 x 64 tiles (4 wavefronts along M: half the dequantization per output
@@ -410,9 +422,24 @@ hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *wq4, const uint1
     // 128 x 64 (also 4 wavefronts along M), else 64 x 64
     const long t256 = (long)((M + 255) / 256) * ((N + 63) / 64);
     const long t128 = (long)((M + 127) / 128) * ((N + 63) / 64);
-    if (t256 >= 256) return launch_tiled<256, 64, 4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-    if (t128 >= 256) return launch_tiled<128, 64, 4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-    return launch_tiled<64, 64, 2>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    if (t256 >= 256) return launch_tiled<256, 64, 4, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    if (t128 >= 256) return launch_tiled<128, 64, 4, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    return launch_tiled<64, 64, 2, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+}
+
+}  // namespace
+
+hipError_t launch_dequant(const uint8_t *wq4, const uint16_t *scales, const uint16_t *zeros, int N,
+                          int K, int G, bool s4, uint16_t *w, hipStream_t stream) {
+    return s4 ? launch_dequant_codes<true>(wq4, scales, zeros, N, K, G, w, stream)
+              : launch_dequant_codes<false>(wq4, scales, zeros, N, K, G, w, stream);
+}
+
+hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
+                       const uint16_t *zeros, int N, int K, int G, bool s4, uint16_t *out,
+                       hipStream_t stream) {
+    return s4 ? launch_gemm_codes<true>(x, M, wq4, scales, zeros, N, K, G, out, stream)
+              : launch_gemm_codes<false>(x, M, wq4, scales, zeros, N, K, G, out, stream);
 }
 
 }  // namespace w4a16

@@ -162,15 +162,18 @@ def pack_u4(q: np.ndarray) -> np.ndarray:
     return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
 
 
-def make_w4a16(M: int, N: int, K: int, G: int = 128, seed: int = 0) -> W4A16Inputs:
-    """X ~ N(0,1) (bf16), u4 codes uniform on 0..15, scales uniform on [0.004, 0.012) and
-    zero points uniform on [6, 9) (both rounded to bf16): the magnitudes of a 4-bit group
+def make_w4a16(M: int, N: int, K: int, G: int = 128, seed: int = 0,
+               signed: bool = False) -> W4A16Inputs:
+    """X ~ N(0,1) (bf16), codes uniform on 0..15, scales uniform on [0.004, 0.012) and
+    zero points uniform on [6, 9) for unsigned codes (u4), on [-1.5, 1.5) for signed ones (s4,
+    the codes read as -8..7), both rounded to bf16: the magnitudes of a 4-bit group
     quantization of N(0, 0.02) weights. Draw order: X, codes, scales, zeros."""
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((M, K), dtype=np.float32)
     q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
     scales = rng.uniform(0.004, 0.012, size=(N, K // G)).astype(np.float32)
-    zeros = rng.uniform(6.0, 9.0, size=(N, K // G)).astype(np.float32)
+    lo, hi = (-1.5, 1.5) if signed else (6.0, 9.0)
+    zeros = rng.uniform(lo, hi, size=(N, K // G)).astype(np.float32)
     return W4A16Inputs(x_bits=f32_to_bf16_bits(x), wq4=pack_u4(q), scales=f32_to_bf16_bits(scales),
                        zeros=f32_to_bf16_bits(zeros), G=G)
 

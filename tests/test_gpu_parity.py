@@ -513,25 +513,26 @@ def _w4a16_dev(inp):
             t(inp.zeros.view(np.int16)).view(torch.bfloat16))
 
 
+@pytest.mark.parametrize("signed", [False, True])
 @pytest.mark.parametrize("N,K,G", [(16, 128, 128), (48, 256, 32), (64, 512, 64), (32, 1024, 256),
                                    (4096, 4096, 128)])
-def test_w4a16_dequant_bit_exact(b, oracle, N, K, G):
-    log(f"w4a16 dequant N={N} K={K} G={G}")
-    inp = make_w4a16(1, N, K, G, seed=N + K + G)
+def test_w4a16_dequant_bit_exact(b, oracle, N, K, G, signed):
+    log(f"w4a16 dequant N={N} K={K} G={G} signed={signed}")
+    inp = make_w4a16(1, N, K, G, seed=N + K + G, signed=signed)
     _, wq4, s, z = _w4a16_dev(inp)
-    got = bf16_bits(b.w4a16_dequant(wq4, s, z))
-    ref = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros)
+    got = bf16_bits(b.w4a16_dequant(wq4, s, z, signed=signed))
+    ref = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros, signed=signed)
     bad = np.argwhere(got != ref)
     assert bad.size == 0, f"{len(bad)} weights differ, first {bad[:4].tolist()}"
 
 
-def _w4a16_case(b, oracle, inp, what, rows=None):
+def _w4a16_case(b, oracle, inp, what, rows=None, signed=False):
     """w4a16_gemm against the oracle: the exact sum of the bf16 products rounded once, with
     |gpu - oracle| <= 1 bf16 ulp + K * 2^-24 * sum_k |x w| (fp32 accumulation); on the
     given rows only (the oracle computes them one by one) when rows is set."""
     x, wq4, s, z = _w4a16_dev(inp)
-    got = bf16_bits(b.w4a16_gemm(x, wq4, s, z))
-    w = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros)
+    got = bf16_bits(b.w4a16_gemm(x, wq4, s, z, signed=signed))
+    w = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros, signed=signed)
     x_bits = inp.x_bits if rows is None else inp.x_bits[rows]
     got = got if rows is None else got[rows]
     ref = oracle.bf16_gemm(x_bits, w)
@@ -559,6 +560,24 @@ def _w4a16_case(b, oracle, inp, what, rows=None):
 def test_w4a16_gemm_shapes(b, oracle, M, N, K, G):
     log(f"w4a16 gemm M={M} N={N} K={K} G={G}")
     _w4a16_case(b, oracle, make_w4a16(M, N, K, G, seed=M + N + K), f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K,G", [(16, 128, 4096, 128), (33, 32, 1024, 256),
+                                     (130, 272, 1024, 64), (400, 4160, 256, 64),
+                                     (1024, 4112, 256, 64)])
+def test_w4a16_gemm_signed_codes(b, oracle, M, N, K, G):
+    """s4 codes on each kernel path (weight streaming, 64x64, 128x64 and 256x64 tiles)."""
+    log(f"w4a16 gemm s4 M={M} N={N} K={K} G={G}")
+    _w4a16_case(b, oracle, make_w4a16(M, N, K, G, seed=M + N + K + 1, signed=True),
+                f"s4 M={M} N={N} K={K}", signed=True)
+
+
+@pytest.mark.parametrize("M", [16, 1024])
+def test_w4a16_gemm_signed_workload(b, oracle, M):
+    log(f"w4a16 s4 workload M={M}")
+    rows = None if M <= 64 else _sampled_rows(M, n=24)
+    _w4a16_case(b, oracle, make_w4a16(M, 4096, 4096, 128, seed=0, signed=True),
+                f"s4 M={M} N=K=4096", rows, signed=True)
 
 
 @pytest.mark.parametrize("M", W4A16_M)
