@@ -424,7 +424,16 @@ def main():
                    "TOPs": round(2.0 * M * N * K / (ms_lib * 1e-3) / 1e12, 1),
                    "w8a8_gemm_speedup": round(ms_lib / ms_gemm, 3)}
 
-    # the addmm epilogue of the BSR kernel (alpha, beta, a per-channel bias)
+    # the addmm epilogue (alpha, beta, a per-channel bias) of the dense and BSR kernels
+    addmm = None
+    if not bsr and not sp24:
+        bias = torch.randn(N, device=dev, dtype=torch.float32) * 0.5
+        ms_addmm = time_median(
+            lambda i: b.w8a8_gemm_addmm(xqs[i % R], sxs[i % R], ws[i % R], d["sw"], bias=bias,
+                                        alpha=0.75, beta=1.5, out=outs[i % R]),
+            args.steps, torch, R, args.eager)
+        addmm = {"kernel": "w8a8_gemm_addmm", "us": round(ms_addmm * 1e3, 3),
+                 "vs_plain": round(ms_addmm / ms_gemm, 3)}
     bsr_addmm = None
     if bsr:
         bias = torch.randn(N, device=dev, dtype=torch.float32) * 0.5
@@ -497,6 +506,8 @@ def main():
         line["gemm_only"]["dense_equivalent_TOPs"] = round(2 * gemm_tops, 1)
     if library is not None:
         line["library_int_mm"] = library
+    if addmm is not None:
+        line["gemm_addmm"] = addmm
     if bsr_addmm is not None:
         line["bsr_addmm"] = bsr_addmm
     if not args.no_decode and name == "prefill_outliers":

@@ -12,6 +12,8 @@ from .oracle import (  # noqa: F401
     decompress24,
     epilogue_addmm_bf16,
     epilogue_bf16,
+    f16_gemm,
+    f16_rne_from_f64,
     gemm_i32,
     load_oracle,
     num_threads,

@@ -59,9 +59,13 @@ def load_oracle():
     lib.oracle_compress24.restype = None
     lib.oracle_decompress24.argtypes = [p, p, i64, i64, p]
     lib.oracle_decompress24.restype = ctypes.c_int
-    lib.oracle_w4a16_dequant.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int, p]
+    lib.oracle_w4a16_dequant.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int, ctypes.c_int, p]
     lib.oracle_w4a16_dequant.restype = None
     lib.oracle_bf16_gemm.argtypes = [p, p, i64, i64, i64, p]
+    lib.oracle_f16_gemm.argtypes = [p, p, i64, i64, i64, p]
+    lib.oracle_f16_gemm.restype = None
+    lib.oracle_f16_rne_from_f64.argtypes = [ctypes.c_double]
+    lib.oracle_f16_rne_from_f64.restype = ctypes.c_uint16
     lib.oracle_bf16_gemm.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -202,10 +206,10 @@ def decompress24(values: np.ndarray, meta: np.ndarray) -> np.ndarray:
 
 
 def w4a16_dequant(wq4: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
-                  signed: bool = False) -> np.ndarray:
+                  signed: bool = False, half: bool = False) -> np.ndarray:
     """Packed 4-bit codes [N,K/2] + bf16 scales/zeros [N,K/G] (bit patterns) -> bf16 w [N,K]
     (bits): w = bf16(bf16(q - z) * s), q the nibble (u4, 0..15) or its 4-bit two's
-    complement (s4, -8..7)."""
+    complement (s4, -8..7); with half, IEEE binary16 in place of bf16 throughout."""
     wq4 = _c(wq4, np.uint8)
     scales = _c(scales, np.uint16)
     zeros = _c(zeros, np.uint16)
@@ -216,7 +220,7 @@ def w4a16_dequant(wq4: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
     G = K // scales.shape[1]
     w = np.empty((N, K), np.uint16)
     load_oracle().oracle_w4a16_dequant(_ptr(wq4), _ptr(scales), _ptr(zeros), N, K, G,
-                                       1 if signed else 0, _ptr(w))
+                                       1 if signed else 0, 1 if half else 0, _ptr(w))
     return w
 
 
@@ -231,6 +235,25 @@ def bf16_gemm(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
     out = np.empty((M, N), np.uint16)
     load_oracle().oracle_bf16_gemm(_ptr(x_bits), _ptr(w_bits), M, N, K, _ptr(out))
     return out
+
+
+def f16_gemm(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 x [M,K] times binary16 w [N,K]^T, summed in float64, rounded once to
+    binary16 (bits)."""
+    x_bits = _c(x_bits, np.uint16)
+    w_bits = _c(w_bits, np.uint16)
+    M, K = x_bits.shape
+    N, K2 = w_bits.shape
+    if K2 != K:
+        raise ValueError("inner dimensions")
+    out = np.empty((M, N), np.uint16)
+    load_oracle().oracle_f16_gemm(_ptr(x_bits), _ptr(w_bits), M, N, K, _ptr(out))
+    return out
+
+
+def f16_rne_from_f64(v: float) -> int:
+    """Bit pattern of the IEEE binary16 nearest to v (ties to even, overflow to infinity)."""
+    return int(load_oracle().oracle_f16_rne_from_f64(float(v)))
 
 
 def num_threads() -> int:

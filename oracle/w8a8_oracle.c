@@ -160,6 +160,43 @@ uint16_t oracle_bf16_rne_from_f64(double v) {
     return (uint16_t)(sign | (uint16_t)((u >> 16) & 0x7FFF));
 }
 
+/*
+ * Round a float64 to the nearest IEEE binary16 (11 significant bits, exponents
+ * -14..15, subnormals kept), ties to even; returns the bit pattern. Values
+ * that round to 2^16 or beyond overflow to infinity. Same construction as the
+ * bf16 rounding above.
+ */
+uint16_t oracle_f16_rne_from_f64(double v) {
+    if (isnan(v)) return 0x7E00;
+    uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return (uint16_t)(sign | 0x7C00);
+    int e;
+    (void)frexp(a, &e);          /* a in [2^(e-1), 2^e) */
+    int unbiased = e - 1;
+    if (unbiased < -14) unbiased = -14; /* subnormal range: fixed quantum 2^-24 */
+    double quantum = ldexp(1.0, unbiased - 10);
+    double r = nearbyint(a / quantum); /* exact division, half to even */
+    double rounded = r * quantum;
+    if (rounded >= 65536.0) return (uint16_t)(sign | 0x7C00);
+    if (rounded < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)r); /* subnormal: r < 1024 */
+    int e2;
+    (void)frexp(rounded, &e2);
+    const int E = e2 - 1;        /* rounded in [2^E, 2^(E+1)) */
+    const uint16_t mant = (uint16_t)((rounded / ldexp(1.0, E) - 1.0) * 1024.0); /* exact */
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | mant);
+}
+
+/* binary16 bit pattern -> float64 (exact). */
+static double f16_to_f64(uint16_t h) {
+    const int ex = (h >> 10) & 31, mant = h & 1023;
+    const double sg = (h & 0x8000) ? -1.0 : 1.0;
+    if (ex == 0) return sg * ldexp((double)mant, -24);
+    if (ex == 31) return mant ? NAN : sg * INFINITY;
+    return sg * ldexp((double)(1024 + mant), ex - 25);
+}
+
 /* out[m,n] = bf16_rne(acc[m,n] * sx[m] * sw[n]); sx*sw is exact in float64. */
 void oracle_epilogue_bf16(const int32_t *acc, const float *sx, const float *sw, int64_t M,
                           int64_t N, uint16_t *out) {
@@ -308,19 +345,30 @@ int oracle_decompress24(const int8_t *values, const uint32_t *meta, int64_t N, i
 /* bf16 bit pattern -> float64 (exact). */
 static double bf16_to_f64(uint16_t bits) { return (double)bf16_bits_to_float(bits); }
 
+/* 16-bit floating-point formats of the W4A16 path: bf16 or IEEE binary16. */
+static double h_to_f64(uint16_t bits, int half) { return half ? f16_to_f64(bits) : bf16_to_f64(bits); }
+static uint16_t h_rne_from_f64(double v, int half) {
+    return half ? oracle_f16_rne_from_f64(v) : oracle_bf16_rne_from_f64(v);
+}
+
 /*
  * W4A16 dequantization. wq4 [N, K/2] bytes: byte j of row n holds code
  * c[n][2j] in its low nibble and c[n][2j+1] in its high nibble; q = c (u4,
  * 0..15) or, with signed_codes, the 4-bit two's complement of c (s4, -8..7).
  * scales, zeros: bf16 [N, K/G]. w [N,K] bf16 (bit patterns):
  *   w[n][k] = bf16(bf16(q - z) * s),  s = scales[n][k/G], z = zeros[n][k/G].
+ * With half, scales, zeros and w are IEEE binary16 and every bf16() above is
+ * a binary16 rounding instead (the page's kernel takes float16 or bfloat16
+ * scales, zeros and activations); the same exactness argument holds with 11
+ * significant bits in place of 8.
  * q - z is exact in float64 unless q != 0 and |z| < 2^-41, where its float64
  * rounding moves it by far less than a bf16 ulp and never onto a bf16 tie, and
  * the product of two bf16 values is exact, so each bf16() here rounds the
  * exact value once.
  */
 void oracle_w4a16_dequant(const uint8_t *wq4, const uint16_t *scales, const uint16_t *zeros,
-                          int64_t N, int64_t K, int64_t G, int signed_codes, uint16_t *w) {
+                          int64_t N, int64_t K, int64_t G, int signed_codes, int half,
+                          uint16_t *w) {
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t k = 0; k < K; ++k) {
@@ -328,10 +376,10 @@ void oracle_w4a16_dequant(const uint8_t *wq4, const uint16_t *scales, const uint
             const int nibble = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
             /* u4: q = nibble in [0, 15]; s4: the nibble's 4-bit two's complement in [-8, 7] */
             const int q = signed_codes && nibble >= 8 ? nibble - 16 : nibble;
-            const double s = bf16_to_f64(scales[n * (K / G) + k / G]);
-            const double z = bf16_to_f64(zeros[n * (K / G) + k / G]);
-            const double shifted = bf16_to_f64(oracle_bf16_rne_from_f64((double)q - z));
-            w[n * K + k] = oracle_bf16_rne_from_f64(shifted * s);
+            const double s = h_to_f64(scales[n * (K / G) + k / G], half);
+            const double z = h_to_f64(zeros[n * (K / G) + k / G], half);
+            const double shifted = h_to_f64(h_rne_from_f64((double)q - z, half), half);
+            w[n * K + k] = h_rne_from_f64(shifted * s, half);
         }
     }
 }
@@ -350,6 +398,20 @@ void oracle_bf16_gemm(const uint16_t *x, const uint16_t *w, int64_t M, int64_t N
             double sum = 0.0;
             for (int64_t k = 0; k < K; ++k) sum += bf16_to_f64(x[m * K + k]) * bf16_to_f64(w[n * K + k]);
             out[m * N + n] = oracle_bf16_rne_from_f64(sum);
+        }
+    }
+}
+
+/* The same product for IEEE binary16 x, w and out. Products of two binary16
+ * values are exact in float64 (22 significant bits). */
+void oracle_f16_gemm(const uint16_t *x, const uint16_t *w, int64_t M, int64_t N, int64_t K,
+                     uint16_t *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) sum += f16_to_f64(x[m * K + k]) * f16_to_f64(w[n * K + k]);
+            out[m * N + n] = oracle_f16_rne_from_f64(sum);
         }
     }
 }

@@ -148,12 +148,14 @@ W4A16_M = [16, 32, 128, 256, 512, 1024]
 
 @dataclass
 class W4A16Inputs:
-    """One synthetic W4A16 layer: bf16 X, packed u4 weights, bf16 group scales and zeros."""
-    x_bits: np.ndarray       # uint16 [M,K], bf16 bit patterns
+    """One synthetic W4A16 layer: bf16 (or binary16) X, packed 4-bit weights, group scales and
+    zeros in the same 16-bit format."""
+    x_bits: np.ndarray       # uint16 [M,K], bf16 (half: binary16) bit patterns
     wq4: np.ndarray          # uint8 [N,K/2]: q[n,2j] in the low nibble of byte j, q[n,2j+1] high
-    scales: np.ndarray       # uint16 [N,K/G], bf16 bit patterns
-    zeros: np.ndarray        # uint16 [N,K/G], bf16 bit patterns
+    scales: np.ndarray       # uint16 [N,K/G], same format
+    zeros: np.ndarray        # uint16 [N,K/G], same format
     G: int
+    half: bool = False
 
 
 def pack_u4(q: np.ndarray) -> np.ndarray:
@@ -163,19 +165,21 @@ def pack_u4(q: np.ndarray) -> np.ndarray:
 
 
 def make_w4a16(M: int, N: int, K: int, G: int = 128, seed: int = 0,
-               signed: bool = False) -> W4A16Inputs:
-    """X ~ N(0,1) (bf16), codes uniform on 0..15, scales uniform on [0.004, 0.012) and
-    zero points uniform on [6, 9) for unsigned codes (u4), on [-1.5, 1.5) for signed ones (s4,
-    the codes read as -8..7), both rounded to bf16: the magnitudes of a 4-bit group
-    quantization of N(0, 0.02) weights. Draw order: X, codes, scales, zeros."""
+               signed: bool = False, half: bool = False) -> W4A16Inputs:
+    """X ~ N(0,1), codes uniform on 0..15, scales uniform on [0.004, 0.012) and zero points
+    uniform on [6, 9) for unsigned codes (u4), on [-1.5, 1.5) for signed ones (s4, the codes
+    read as -8..7), X, scales and zeros rounded to bf16 (half: to IEEE binary16): the
+    magnitudes of a 4-bit group quantization of N(0, 0.02) weights. Draw order: X, codes,
+    scales, zeros."""
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((M, K), dtype=np.float32)
     q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
     scales = rng.uniform(0.004, 0.012, size=(N, K // G)).astype(np.float32)
     lo, hi = (-1.5, 1.5) if signed else (6.0, 9.0)
     zeros = rng.uniform(lo, hi, size=(N, K // G)).astype(np.float32)
-    return W4A16Inputs(x_bits=f32_to_bf16_bits(x), wq4=pack_u4(q), scales=f32_to_bf16_bits(scales),
-                       zeros=f32_to_bf16_bits(zeros), G=G)
+    to16 = (lambda a: a.astype(np.float16).view(np.uint16)) if half else f32_to_bf16_bits
+    return W4A16Inputs(x_bits=to16(x), wq4=pack_u4(q), scales=to16(scales), zeros=to16(zeros),
+                       G=G, half=half)
 
 
 def make_w4a16_inputs(name: str, seed: int = 0, M: int | None = None) -> W4A16Inputs:

@@ -1,6 +1,6 @@
 """Exact rational arithmetic used to pin the oracle (test helper).
 
-Binary32 and bf16 rounding are written out here from their definition
+Binary32, bf16 and binary16 rounding are written out here from their definition
 (nearest representable value, ties to the even significand, subnormals kept),
 on Python Fractions. Nothing here calls the C oracle or the hardware's float
 unit, so a slip in either (a contracted or double-precision division, a
@@ -36,6 +36,13 @@ def f32(v: Fraction) -> Fraction:
 
 def bf16(v: Fraction) -> Fraction:
     return round_to_format(v, 7)
+
+
+def f16(v: Fraction) -> Fraction:
+    """IEEE binary16: 10 stored fraction bits, exponents from -14 (subnormals below).
+    Values rounding to 2^16 or beyond overflow (returned as None)."""
+    r = round_to_format(v, 10, emin=-14)
+    return None if abs(r) >= 2 ** 16 else r
 
 
 def quantize_row(xs):

@@ -14,6 +14,7 @@ import pytest
 import torch
 
 from exact import bf16 as exact_bf16
+from exact import f16 as exact_f16
 from exact import quantize_row as exact_quantize_row
 from quantized_gemm_quantize_amd.inputs import (bf16_bits_to_f32, bsr_from_dense, dense_from_bsr,
                                                 f32_to_bf16_bits, make_inputs, make_linear)
@@ -449,6 +450,77 @@ def test_w4a16_dequant_signed_hand_worked(oracle):
                              signed=True)
     assert w[0].tolist() == [int(c["w_bits"], 16)] * 2
     assert float(bf16_bits_to_f32(w)[0, 0]) == c["w"]
+
+
+def _f16_to_fraction(bits: int) -> Fraction:
+    """IEEE binary16 bit pattern -> exact value (finite patterns), from the format's layout."""
+    e, m = (bits >> 10) & 31, bits & 1023
+    v = Fraction(m, 2 ** 24) if e == 0 else Fraction(1024 + m, 2 ** 25) * Fraction(2) ** e
+    return -v if bits & 0x8000 else v
+
+
+def test_f16_rounding_matches_exact(oracle):
+    """The oracle's binary16 rounding against the exact rounding on a spread of values:
+    normals, subnormals, ties (both parities), the largest finite value and overflow."""
+    vals = [0.0, 1.0, -1.0, 0.1, 1 / 3, 65504.0, 65519.99, 65520.0, 2.0 ** -24, 2.0 ** -25,
+            3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11,
+            -7.3125 * 41 / 4096, 15 - 2.0 ** -11, 1e-8, 12345.678]
+    rng = np.random.default_rng(17)
+    vals += list(rng.standard_normal(200) * np.exp2(rng.integers(-20, 15, 200)))
+    for v in vals:
+        bits = oracle.f16_rne_from_f64(v)
+        ref = exact_f16(Fraction(v))
+        if ref is None:
+            assert bits & 0x7FFF == 0x7C00, v          # infinity
+        else:
+            assert _f16_to_fraction(bits) == ref, v
+            if ref == 0:
+                assert bits & 0x7FFF == 0
+
+
+def test_w4a16_dequant_f16_hand_worked(oracle):
+    """binary16 scales, zeros and weights: the worked cases of the fixture."""
+    g = _load("w4a16_worked.json")
+    for case in ("f16_shift_rounding", "f16_rounding"):
+        c = g[case]
+        wq4 = np.array([[c["q"] | (c["q"] << 4)]], np.uint8)
+        w = oracle.w4a16_dequant(wq4, _bits(c["scale_bits"])[None, :],
+                                 _bits(c["zero_bits"])[None, :], half=True)
+        assert w[0].tolist() == [int(c["w_bits"], 16)] * 2, case
+        assert float(_f16_to_fraction(int(w[0, 0]))) == c["w"]
+
+
+@pytest.mark.parametrize("signed", [False, True])
+def test_w4a16_dequant_f16_matches_exact_rationals(oracle, signed):
+    """Every binary16 dequantized weight of a random layer against f16(f16(q - z) * s) on
+    exact rationals."""
+    from quantized_gemm_quantize_amd.inputs import make_w4a16
+    inp = make_w4a16(1, 6, 256, G=64, seed=19, signed=signed, half=True)
+    w = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros, signed=signed, half=True)
+    q = np.empty((6, 256), np.int64)
+    q[:, 0::2] = inp.wq4 & 15
+    q[:, 1::2] = inp.wq4 >> 4
+    if signed:
+        q = np.where(q >= 8, q - 16, q)
+    for n in range(6):
+        for k in range(256):
+            sv = _f16_to_fraction(int(inp.scales[n, k // 64]))
+            zv = _f16_to_fraction(int(inp.zeros[n, k // 64]))
+            ref = exact_f16(exact_f16(int(q[n, k]) - zv) * sv)
+            assert _f16_to_fraction(int(w[n, k])) == ref, (n, k)
+
+
+def test_f16_gemm_matches_exact_sums(oracle):
+    """The binary16 product against the exact rational sum rounded once (brute force)."""
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((3, 40)).astype(np.float16)
+    w = (rng.standard_normal((4, 40)) * 0.05).astype(np.float16)
+    out = oracle.f16_gemm(x.view(np.uint16), w.view(np.uint16))
+    for m in range(3):
+        for n in range(4):
+            exact = sum(_f16_to_fraction(int(x.view(np.uint16)[m, k])) *
+                        _f16_to_fraction(int(w.view(np.uint16)[n, k])) for k in range(40))
+            assert _f16_to_fraction(int(out[m, n])) == exact_f16(exact), (m, n)
 
 
 def test_w4a16_dequant_signed_agrees_below_eight(oracle):
