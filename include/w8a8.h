@@ -235,44 +235,52 @@ w8a8_status w8a8_sparse24_gemm(const int8_t *xq, const float *x_scale, int64_t M
                                void *stream);
 
 /*
- * W4A16: asymmetric group-wise 4-bit weights with bf16 activations (pytorch/ao
- * PR #153, fused HQQ quantization GEMM: u4 / s4 weights upcast to bf16, scaled
- * and shifted group-wise by bf16 scales and zero points along K, then the GEMM).
+ * W4A16: asymmetric group-wise 4-bit weights with 16-bit activations
+ * (pytorch/ao PR #153, fused HQQ quantization GEMM: u4 / s4 weights upcast to
+ * bfloat16 or float16, scaled and shifted group-wise by scales and zero points
+ * of that type along K, then the GEMM). x, scales, zeros, w and out share one
+ * 16-bit format: W4A16_BF16 or W4A16_F16 (IEEE binary16); every rounding
+ * below is to that format.
  *   wq4     [N, K/2] uint8: byte j of row n holds code c[n][2j] in its low
  *           nibble and c[n][2j+1] in its high nibble; q = c with
  *           W4A16_CODES_U4 (0..15), its 4-bit two's complement with
  *           W4A16_CODES_S4 (-8..7)
- *   scales, zeros [N, K/G] bf16 (bit patterns), G = group_size
+ *   scales, zeros [N, K/G] 16-bit values (bit patterns), G = group_size
  *   w[n][k] = bf16(bf16(q[n][k] - zeros[n][k/G]) * scales[n][k/G])
  *           (each operation rounded to nearest-even bf16, as elementwise bf16
  *           arithmetic does)
  * N a positive multiple of 16, K a positive multiple of 128, G a positive
  * multiple of 32 dividing K; wq4, x, w and out 16-byte aligned, scales and
- * zeros 2-byte aligned. An unknown codes value is W8A8_ERR_DTYPE.
+ * zeros 2-byte aligned. An unknown codes or dtype value is W8A8_ERR_DTYPE.
  */
 typedef enum {
     W4A16_CODES_U4 = 0, /* unsigned codes, q in 0..15 */
     W4A16_CODES_S4 = 1  /* signed codes, q in -8..7 (4-bit two's complement) */
 } w4a16_codes;
+typedef enum {
+    W4A16_BF16 = 0, /* bfloat16 */
+    W4A16_F16 = 1   /* IEEE binary16 (subnormals kept) */
+} w4a16_dtype;
 
-/* Dequantized weights: w [N,K] bf16, bit-exact to the definition above (the
+/* Dequantized weights: w [N,K], bit-exact to the definition above (the
  * standalone dequantization the pages list next to the fused kernel). */
 w8a8_status w4a16_dequant(const uint8_t *wq4, const void *scales, const void *zeros, int64_t N,
-                          int64_t K, int64_t group_size, w4a16_codes codes, void *w,
-                          void *stream);
+                          int64_t K, int64_t group_size, w4a16_codes codes, w4a16_dtype dtype,
+                          void *w, void *stream);
 
 /*
- * Fused dequant GEMM: out[m][n] = bf16(sum_k x[m][k] * w[n][k]) with x bf16
- * [M,K] row-major, out bf16 [M,N] row-major, the products accumulated in
- * fp32 (within one bf16 ulp plus the fp32 summation error of the exact sum).
+ * Fused dequant GEMM: out[m][n] = round(sum_k x[m][k] * w[n][k]) with x
+ * [M,K] row-major, out [M,N] row-major, the products accumulated in fp32
+ * (within one ulp of the format plus the fp32 summation error of the exact
+ * sum).
  * The dequantized weights never leave the chip. M >= 0: M <= 64 streams the
  * weights once (dequantized in registers); larger M takes LDS tiles, each
  * tile dequantizing its weight columns once for all of its rows.
- * Errors: NULL, SHAPE, ALIGN, DTYPE (codes), HIP.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE (codes, dtype), HIP.
  */
 w8a8_status w4a16_gemm(const void *x, int64_t M, const uint8_t *wq4, const void *scales,
                        const void *zeros, int64_t N, int64_t K, int64_t group_size,
-                       w4a16_codes codes, void *out, void *stream);
+                       w4a16_codes codes, w4a16_dtype dtype, void *out, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *w8a8_status_string(int status);

@@ -62,8 +62,8 @@ def load():
     lib.w8a8_fused_linear.argtypes = [p, i64, i64, p, p, i64, p, f32, f32, p, p]
     lib.w8a8_compress24.argtypes = [p, i64, i64, p, p, p]
     lib.w8a8_sparse24_gemm.argtypes = [p, p, i64, p, p, p, i64, i64, p, i32, p]
-    lib.w4a16_dequant.argtypes = [p, p, p, i64, i64, i64, i32, p, p]
-    lib.w4a16_gemm.argtypes = [p, i64, p, p, p, i64, i64, i64, i32, p, p]
+    lib.w4a16_dequant.argtypes = [p, p, p, i64, i64, i64, i32, i32, p, p]
+    lib.w4a16_gemm.argtypes = [p, i64, p, p, p, i64, i64, i64, i32, i32, p, p]
     for fn in ("w8a8_quantize_rows", "w8a8_quantize_rows_f32", "w8a8_gemm", "w8a8_gemm_addmm",
                "w8a8_fused_linear", "w8a8_bsr_gemm", "w8a8_bsr_gemm_addmm", "w8a8_compress24",
                "w8a8_sparse24_gemm",
@@ -223,45 +223,62 @@ def w8a8_sparse24_gemm(xq, x_scale, values, meta, w_scale, out=None, out_dtype="
 
 
 def _w4a16_operands(wq4, scales, zeros):
+    """Shapes and the 16-bit format (from the scales: bfloat16 or float16) of a W4A16 weight."""
     _check_tensor(wq4, "wq4", torch.uint8, 2)
-    _check_tensor(scales, "scales", torch.bfloat16, 2)
-    _check_tensor(zeros, "zeros", torch.bfloat16, 2)
+    dt = scales.dtype if isinstance(scales, torch.Tensor) else None
+    if dt not in (torch.bfloat16, torch.float16):
+        raise TypeError("scales must be a bfloat16 or float16 tensor")
+    _check_tensor(scales, "scales", dt, 2)
+    _check_tensor(zeros, "zeros", dt, 2)
     N, K2 = wq4.shape
     K = 2 * K2
     if scales.shape != zeros.shape or scales.shape[0] != N or scales.shape[1] == 0 \
             or K % scales.shape[1]:
         raise ValueError("W4A16 operand shapes")
-    return N, K, K // scales.shape[1]
+    return N, K, K // scales.shape[1], dt
+
+
+W4A16_BF16, W4A16_F16 = 0, 1
+
+
+def _w4a16_dtype(dt) -> int:
+    return W4A16_F16 if dt == torch.float16 else W4A16_BF16
 
 
 W4A16_CODES_U4, W4A16_CODES_S4 = 0, 1
 
 
 def w4a16_dequant(wq4, scales, zeros, signed=False, out=None, stream=None):
-    """Packed 4-bit codes [N,K/2] + bf16 scales/zeros [N,K/G] -> bf16 w [N,K] =
-    bf16(bf16(q - z) * s); q the code (u4) or, with signed, its 4-bit two's complement (s4)."""
-    N, K, G = _w4a16_operands(wq4, scales, zeros)
+    """Packed 4-bit codes [N,K/2] + scales/zeros [N,K/G] (bfloat16 or float16) -> w [N,K] of
+    that type = round(round(q - z) * s); q the code (u4) or, with signed, its 4-bit two's
+    complement (s4)."""
+    N, K, G, dt = _w4a16_operands(wq4, scales, zeros)
     if out is None:
-        out = torch.empty((N, K), dtype=torch.bfloat16, device=wq4.device)
-    _check_tensor(out, "out", torch.bfloat16, 2)
+        out = torch.empty((N, K), dtype=dt, device=wq4.device)
+    _check_tensor(out, "out", dt, 2)
     if tuple(out.shape) != (N, K):
         raise ValueError("out shape")
     _call("w4a16_dequant", wq4.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K, G,
-          W4A16_CODES_S4 if signed else W4A16_CODES_U4, out.data_ptr(), _stream_handle(stream))
+          W4A16_CODES_S4 if signed else W4A16_CODES_U4, _w4a16_dtype(dt), out.data_ptr(),
+          _stream_handle(stream))
     return out
 
 
 def w4a16_gemm(x, wq4, scales, zeros, signed=False, out=None, stream=None):
-    """out [M,N] bf16 = x [M,K] bf16 times the dequantized 4-bit weights (u4, or s4 with
-    signed), fused."""
-    _check_tensor(x, "x", torch.bfloat16, 2)
-    N, K, G = _w4a16_operands(wq4, scales, zeros)
+    """out [M,N] = x [M,K] times the dequantized 4-bit weights (u4, or s4 with signed), fused;
+    x, scales, zeros and out all bfloat16 or all float16."""
+    N, K, G, dt = _w4a16_operands(wq4, scales, zeros)
+    _check_tensor(x, "x", dt, 2)
     M = x.shape[0]
     if x.shape[1] != K:
         raise ValueError("operand shapes")
-    out = _out(out, M, N, _out_dtype("bf16"), x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=x.device)
+    _check_tensor(out, "out", dt, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out shape")
     _call("w4a16_gemm", x.data_ptr(), M, wq4.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N,
-          K, G, W4A16_CODES_S4 if signed else W4A16_CODES_U4, out.data_ptr(),
+          K, G, W4A16_CODES_S4 if signed else W4A16_CODES_U4, _w4a16_dtype(dt), out.data_ptr(),
           _stream_handle(stream))
     return out
 

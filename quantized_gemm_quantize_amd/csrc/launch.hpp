@@ -47,13 +47,14 @@ hipError_t launch_bsr_gemm(const int8_t *xq, const float *xs, int M, int K, cons
 
 namespace w4a16 {
 
-// W4A16 (bf16 bit patterns as uint16_t): standalone dequantization of packed
-// 4-bit weights [N,K/2] (u4, or s4 when s4) with bf16 scales/zeros [N,K/G]
-// into bf16 w [N,K], and the fused dequant GEMM out [M,N] = bf16(x [M,K] . w^T).
+// W4A16 (16-bit values as uint16_t bit patterns: bf16, or binary16 when f16):
+// standalone dequantization of packed 4-bit weights [N,K/2] (u4, or s4 when
+// s4) with scales/zeros [N,K/G] into w [N,K], and the fused dequant GEMM
+// out [M,N] = round(x [M,K] . w^T).
 hipError_t launch_dequant(const uint8_t *wq4, const uint16_t *scales, const uint16_t *zeros, int N,
-                          int K, int G, bool s4, uint16_t *w, hipStream_t stream);
+                          int K, int G, bool s4, bool f16, uint16_t *w, hipStream_t stream);
 hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
-                       const uint16_t *zeros, int N, int K, int G, bool s4, uint16_t *out,
-                       hipStream_t stream);
+                       const uint16_t *zeros, int N, int K, int G, bool s4, bool f16,
+                       uint16_t *out, hipStream_t stream);
 
 }  // namespace w4a16

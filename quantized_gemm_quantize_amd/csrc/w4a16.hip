@@ -32,10 +32,60 @@ __device__ __forceinline__ float bf16_to_float(uint16_t bits) {
     return __uint_as_float((uint32_t)bits << 16);
 }
 
+// The 16-bit format of activations, scales, zeros, weights and outputs: bf16,
+// or IEEE binary16 with F16 (the page's kernel takes either). Conversions from
+// fp32 round to nearest even, subnormals kept.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+template <bool F16>
+__device__ __forceinline__ float h_to_float(uint16_t bits) {
+    if constexpr (F16)
+        return (float)__builtin_bit_cast(_Float16, bits);
+    else
+        return bf16_to_float(bits);
+}
+
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+    if constexpr (F16)
+        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+    else
+        return pack_bf16x2(lo, hi);
+}
+
+template <bool F16>
+__device__ __forceinline__ float h_lo(uint32_t w) {
+    if constexpr (F16)
+        return h_to_float<true>((uint16_t)(w & 0xFFFFu));
+    else
+        return bf16_lo(w);
+}
+
+template <bool F16>
+__device__ __forceinline__ float h_hi(uint32_t w) {
+    if constexpr (F16)
+        return h_to_float<true>((uint16_t)(w >> 16));
+    else
+        return bf16_hi(w);
+}
+
+// MFMAs on 8 packed 16-bit values per lane (weights first), fp32 accumulation.
+template <bool F16>
+__device__ __forceinline__ v4f mfma16x16x32(uint4 a, uint4 b, v4f c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
+                                                      __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                       __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
 // 8 codes (code e in bits 4e .. 4e+3) -> 8 bf16 weights, packed 2 per word.
 // S4: signed codes. c ^ 8 is q + 8 in 0..15, converted like an unsigned code;
-// subtracting 8 is exact, so q - z still takes a single rounding.
-template <bool S4>
+// subtracting 8 is exact, so q - z still takes a single rounding. F16: the
+// roundings and the result are binary16 instead of bf16.
+template <bool S4, bool F16>
 __device__ __forceinline__ uint4 dequant8(uint32_t packed, float s, float z) {
     if constexpr (S4) packed ^= 0x88888888u;
     uint32_t even = packed & 0x0F0F0F0Fu, odd = (packed >> 4) & 0x0F0F0F0Fu;
@@ -56,14 +106,14 @@ __device__ __forceinline__ uint4 dequant8(uint32_t packed, float s, float z) {
     uint32_t o[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-        const uint32_t shifted = pack_bf16x2(d[2 * h], d[2 * h + 1]);   // bf16(q - z)
-        o[h] = pack_bf16x2(bf16_lo(shifted) * s, bf16_hi(shifted) * s);
+        const uint32_t shifted = pack_h2<F16>(d[2 * h], d[2 * h + 1]);   // bf16(q - z)
+        o[h] = pack_h2<F16>(h_lo<F16>(shifted) * s, h_hi<F16>(shifted) * s);
     }
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // One thread per 8 weights: w [N,K] bf16.
-template <bool S4>
+template <bool S4, bool F16>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict__ wq4,
                                                        const uint16_t *__restrict__ scales,
                                                        const uint16_t *__restrict__ zeros,
@@ -75,7 +125,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict
     const int64_t n = k8 / K;
     const int k = (int)(k8 % K);
     const int64_t gi = n * (K / G) + k / G;
-    w[t] = dequant8<S4>(wq4[t], bf16_to_float(scales[gi]), bf16_to_float(zeros[gi]));
+    w[t] = dequant8<S4, F16>(wq4[t], h_to_float<F16>(scales[gi]), h_to_float<F16>(zeros[gi]));
 }
 
 // Weight-streaming W4A16 GEMM for M <= 64: one workgroup per 16 output
@@ -87,7 +137,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict
 // of 8 columns (the same permutation of K on both operands).
 constexpr int kSplit = 8;
 
-template <int MT, bool S4>
+template <int MT, bool S4, bool F16>
 __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_kernel(
     const uint16_t *__restrict__ X, const uint8_t *__restrict__ wq4,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -114,7 +164,7 @@ __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_kernel(
     for (int c = c_begin; c < c_end; ++c) {
         const uint4 codes = *reinterpret_cast<const uint4 *>(wrow + 64 * c);
         const int g = (128 * c + 32 * q) / G;
-        const float s = bf16_to_float(srow[g]), z = bf16_to_float(zrow[g]);
+        const float s = h_to_float<F16>(srow[g]), z = h_to_float<F16>(zrow[g]);
         uint4 xv[MT][4];
 #pragma unroll
         for (int mb = 0; mb < MT; ++mb)
@@ -123,11 +173,10 @@ __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_kernel(
         const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const v8bf a = __builtin_bit_cast(v8bf, dequant8<S4>(cw[t], s, z));
+            const uint4 a = dequant8<S4, F16>(cw[t], s, z);
 #pragma unroll
             for (int mb = 0; mb < MT; ++mb)
-                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    a, __builtin_bit_cast(v8bf, xv[mb][t]), acc[mb], 0, 0, 0);
+                acc[mb] = mfma16x16x32<F16>(a, xv[mb][t], acc[mb]);
         }
     }
 
@@ -147,16 +196,16 @@ __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_kernel(
         float sum = 0.0f;
 #pragma unroll
         for (int w = 0; w < kSplit; ++w) sum += red[w][mb][r][l];
-        out[(int64_t)m * N + n0 + ch] = (uint16_t)(pack_bf16x2(sum, 0.0f) & 0xFFFFu);
+        out[(int64_t)m * N + n0 + ch] = (uint16_t)(pack_h2<F16>(sum, 0.0f) & 0xFFFFu);
     }
 }
 
-template <int MT, bool S4>
+template <int MT, bool S4, bool F16>
 hipError_t launch_decode_mt(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
                             const uint16_t *zeros, int N, int K, int G, uint16_t *out,
                             hipStream_t stream) {
     const int chunks_per_wave = (K / 128 + kSplit - 1) / kSplit;
-    w4a16_decode_kernel<MT, S4><<<dim3((unsigned)(N / 16)), dim3(kSplit * kWave), 0, stream>>>(
+    w4a16_decode_kernel<MT, S4, F16><<<dim3((unsigned)(N / 16)), dim3(kSplit * kWave), 0, stream>>>(
         x, wq4, scales, zeros, out, M, N, K, G, chunks_per_wave);
     return hipGetLastError();
 }
@@ -181,7 +230,7 @@ typedef __attribute__((address_space(1))) void global_void;
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int BM, int BN, int WAVES_M, bool S4>
+template <int BM, int BN, int WAVES_M, bool S4, bool F16>
 __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ X, const uint8_t *__restrict__ wq4,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -253,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
     // word i of a thread's codes, dequantized into its weight buffer slot
     auto store_word = [&](const Codes &c, int i, uint4 *__restrict__ wb) {
         wb[wr * 8 + ((part * (CODES / 8) + i) ^ swz(wr))] =
-            dequant8<S4>(c.c[i], bf16_to_float(c.s), bf16_to_float(c.z));
+            dequant8<S4, F16>(c.c[i], h_to_float<F16>(c.s), h_to_float<F16>(c.z));
     };
     auto load_x = [&](int j, uint4 *__restrict__ buf) {
 #pragma unroll
@@ -276,18 +325,23 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int c = (2 * u + kh) ^ fswz;
-            v8bf xa[TM], wf[TN];
+            uint4 xa[TM], wf[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                xa[i] = __builtin_bit_cast(v8bf, xb[(wm * WM + 32 * i + frag_row) * 8 + c]);
+                xa[i] = xb[(wm * WM + 32 * i + frag_row) * 8 + c];
 #pragma unroll
             for (int q = 0; q < TN; ++q)
-                wf[q] = __builtin_bit_cast(v8bf, wb[(wn * WN + 32 * q + frag_row) * 8 + c]);
+                wf[q] = wb[(wn * WN + 32 * q + frag_row) * 8 + c];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int q = 0; q < TN; ++q)
-                    acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[q], xa[i], acc[i][q], 0, 0, 0);
+                    acc[i][q] = F16 ? __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                          __builtin_bit_cast(v8h, wf[q]), __builtin_bit_cast(v8h, xa[i]),
+                                          acc[i][q], 0, 0, 0)
+                                    : __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                          __builtin_bit_cast(v8bf, wf[q]), __builtin_bit_cast(v8bf, xa[i]),
+                                          acc[i][q], 0, 0, 0);
             // this step's share of the code words (one or two; none in the
             // last steps when there are only two)
             constexpr int WPS = CODES / 8 > 4 ? CODES / 32 : 1;
@@ -370,8 +424,8 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
             for (int g = 0; g < 4; ++g) {
                 const int ml = i * 32 + frag_row;
                 const v16f &a = acc[i][j];
-                const uint32_t lo = pack_bf16x2(a[4 * g], a[4 * g + 1]);
-                const uint32_t hi = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
+                const uint32_t lo = pack_h2<F16>(a[4 * g], a[4 * g + 1]);
+                const uint32_t hi = pack_h2<F16>(a[4 * g + 2], a[4 * g + 3]);
                 st8[(ml * CH + ((j * 4 + g) ^ (ml & PM))) * 2 + kh] = make_uint2(lo, hi);
             }
     __syncthreads();
@@ -386,35 +440,35 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
     }
 }
 
-template <int BM, int BN, int WAVES_M, bool S4>
+template <int BM, int BN, int WAVES_M, bool S4, bool F16>
 hipError_t launch_tiled(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
                         const uint16_t *zeros, int N, int K, int G, uint16_t *out,
                         hipStream_t stream) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    w4a16_tiled_kernel<BM, BN, WAVES_M, S4><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream>>>(
+    w4a16_tiled_kernel<BM, BN, WAVES_M, S4, F16><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream>>>(
         x, wq4, scales, zeros, out, M, N, K, G, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
-template <bool S4>
+template <bool S4, bool F16>
 hipError_t launch_dequant_codes(const uint8_t *wq4, const uint16_t *scales, const uint16_t *zeros,
                                 int N, int K, int G, uint16_t *w, hipStream_t stream) {
     const int64_t words = (int64_t)N * K / 8;
-    dequant_kernel<S4><<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream>>>(
+    dequant_kernel<S4, F16><<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream>>>(
         reinterpret_cast<const uint32_t *>(wq4), scales, zeros, words, K, G,
         reinterpret_cast<uint4 *>(w));
     return hipGetLastError();
 }
 
-template <bool S4>
+template <bool S4, bool F16>
 hipError_t launch_gemm_codes(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
                              const uint16_t *zeros, int N, int K, int G, uint16_t *out,
                              hipStream_t stream) {
     switch ((M + 15) / 16) {
-        case 1: return launch_decode_mt<1, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-        case 2: return launch_decode_mt<2, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-        case 3: return launch_decode_mt<3, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-        case 4: return launch_decode_mt<4, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+        case 1: return launch_decode_mt<1, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+        case 2: return launch_decode_mt<2, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+        case 3: return launch_decode_mt<3, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+        case 4: return launch_decode_mt<4, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
         default: break;
     }
     // 256 x 64 tiles (4 wavefronts along M: half the dequantization per output
@@ -422,24 +476,30 @@ hipError_t launch_gemm_codes(const uint16_t *x, int M, const uint8_t *wq4, const
     // 128 x 64 (also 4 wavefronts along M), else 64 x 64
     const long t256 = (long)((M + 255) / 256) * ((N + 63) / 64);
     const long t128 = (long)((M + 127) / 128) * ((N + 63) / 64);
-    if (t256 >= 256) return launch_tiled<256, 64, 4, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-    if (t128 >= 256) return launch_tiled<128, 64, 4, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-    return launch_tiled<64, 64, 2, S4>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    if (t256 >= 256) return launch_tiled<256, 64, 4, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    if (t128 >= 256) return launch_tiled<128, 64, 4, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    return launch_tiled<64, 64, 2, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
 }
 
 }  // namespace
 
 hipError_t launch_dequant(const uint8_t *wq4, const uint16_t *scales, const uint16_t *zeros, int N,
-                          int K, int G, bool s4, uint16_t *w, hipStream_t stream) {
-    return s4 ? launch_dequant_codes<true>(wq4, scales, zeros, N, K, G, w, stream)
-              : launch_dequant_codes<false>(wq4, scales, zeros, N, K, G, w, stream);
+                          int K, int G, bool s4, bool f16, uint16_t *w, hipStream_t stream) {
+    if (f16)
+        return s4 ? launch_dequant_codes<true, true>(wq4, scales, zeros, N, K, G, w, stream)
+                  : launch_dequant_codes<false, true>(wq4, scales, zeros, N, K, G, w, stream);
+    return s4 ? launch_dequant_codes<true, false>(wq4, scales, zeros, N, K, G, w, stream)
+              : launch_dequant_codes<false, false>(wq4, scales, zeros, N, K, G, w, stream);
 }
 
 hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
-                       const uint16_t *zeros, int N, int K, int G, bool s4, uint16_t *out,
-                       hipStream_t stream) {
-    return s4 ? launch_gemm_codes<true>(x, M, wq4, scales, zeros, N, K, G, out, stream)
-              : launch_gemm_codes<false>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+                       const uint16_t *zeros, int N, int K, int G, bool s4, bool f16,
+                       uint16_t *out, hipStream_t stream) {
+    if (f16)
+        return s4 ? launch_gemm_codes<true, true>(x, M, wq4, scales, zeros, N, K, G, out, stream)
+                  : launch_gemm_codes<false, true>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    return s4 ? launch_gemm_codes<true, false>(x, M, wq4, scales, zeros, N, K, G, out, stream)
+              : launch_gemm_codes<false, false>(x, M, wq4, scales, zeros, N, K, G, out, stream);
 }
 
 }  // namespace w4a16

@@ -227,26 +227,28 @@ static w8a8_status w4a16_shape(int64_t N, int64_t K, int64_t G) {
 static bool misaligned2(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 1u) != 0; }
 
 w8a8_status w4a16_dequant(const uint8_t *wq4, const void *scales, const void *zeros, int64_t N,
-                          int64_t K, int64_t group_size, w4a16_codes codes, void *w,
-                          void *stream) {
+                          int64_t K, int64_t group_size, w4a16_codes codes, w4a16_dtype dtype,
+                          void *w, void *stream) {
     if (w8a8_status s = w4a16_shape(N, K, group_size)) return s;
     if (codes != W4A16_CODES_U4 && codes != W4A16_CODES_S4) return W8A8_ERR_DTYPE;
+    if (dtype != W4A16_BF16 && dtype != W4A16_F16) return W8A8_ERR_DTYPE;
     if (!wq4 || !scales || !zeros || !w) return W8A8_ERR_NULL;
     if (misaligned(wq4) || misaligned(w) || misaligned2(scales) || misaligned2(zeros))
         return W8A8_ERR_ALIGN;
     return hip_status(w4a16::launch_dequant(wq4, static_cast<const uint16_t *>(scales),
                                             static_cast<const uint16_t *>(zeros), (int)N, (int)K,
                                             (int)group_size, codes == W4A16_CODES_S4,
-                                            static_cast<uint16_t *>(w),
+                                            dtype == W4A16_F16, static_cast<uint16_t *>(w),
                                             static_cast<hipStream_t>(stream)));
 }
 
 w8a8_status w4a16_gemm(const void *x, int64_t M, const uint8_t *wq4, const void *scales,
                        const void *zeros, int64_t N, int64_t K, int64_t group_size,
-                       w4a16_codes codes, void *out, void *stream) {
+                       w4a16_codes codes, w4a16_dtype dtype, void *out, void *stream) {
     if (M < 0 || M > INT_MAX / 2) return W8A8_ERR_SHAPE;
     if (w8a8_status s = w4a16_shape(N, K, group_size)) return s;
     if (codes != W4A16_CODES_U4 && codes != W4A16_CODES_S4) return W8A8_ERR_DTYPE;
+    if (dtype != W4A16_BF16 && dtype != W4A16_F16) return W8A8_ERR_DTYPE;
     if ((M + 63) / 64 > INT_MAX / ((N + 63) / 64)) return W8A8_ERR_SHAPE;  // grid.x
     if (M == 0) return W8A8_OK;
     if (!x || !wq4 || !scales || !zeros || !out) return W8A8_ERR_NULL;
@@ -257,7 +259,7 @@ w8a8_status w4a16_gemm(const void *x, int64_t M, const uint8_t *wq4, const void 
                                          static_cast<const uint16_t *>(scales),
                                          static_cast<const uint16_t *>(zeros), (int)N, (int)K,
                                          (int)group_size, codes == W4A16_CODES_S4,
-                                         static_cast<uint16_t *>(out),
+                                         dtype == W4A16_F16, static_cast<uint16_t *>(out),
                                          static_cast<hipStream_t>(stream)));
 }
 

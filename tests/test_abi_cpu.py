@@ -50,6 +50,8 @@ def test_header_constants_match_binding():
     assert f"#define W8A8_FUSED_MAX_M {binding.W8A8_FUSED_MAX_M}" in text
     assert re.search(rf"W4A16_CODES_U4\s*=\s*{binding.W4A16_CODES_U4}\b", text)
     assert re.search(rf"W4A16_CODES_S4\s*=\s*{binding.W4A16_CODES_S4}\b", text)
+    assert re.search(rf"W4A16_BF16\s*=\s*{binding.W4A16_BF16}\b", text)
+    assert re.search(rf"W4A16_F16\s*=\s*{binding.W4A16_F16}\b", text)
     assert 127 * 127 * binding.W8A8_MAX_K < 2 ** 31
     assert 127 * 127 * (binding.W8A8_MAX_K + 16) >= 2 ** 31
     for name in ("W8A8_ERR_NULL", "W8A8_ERR_SHAPE", "W8A8_ERR_ALIGN", "W8A8_ERR_K_OVERFLOW",
@@ -172,11 +174,11 @@ def test_sparse24_gemm_validation(lib):
 def test_w4a16_validation(lib):
     d, g = lib.w4a16_dequant, lib.w4a16_gemm
     dargs = lambda **kw: [kw.get("wq", P), kw.get("s", P), kw.get("z", P), kw.get("N", 64),
-                          kw.get("K", 256), kw.get("G", 128), kw.get("codes", 0), kw.get("w", P),
-                          None]
+                          kw.get("K", 256), kw.get("G", 128), kw.get("codes", 0), kw.get("dt", 0),
+                          kw.get("w", P), None]
     gargs = lambda **kw: [kw.get("x", P), kw.get("M", 16), kw.get("wq", P), kw.get("s", P),
                           kw.get("z", P), kw.get("N", 64), kw.get("K", 256), kw.get("G", 128),
-                          kw.get("codes", 0), kw.get("out", P), None]
+                          kw.get("codes", 0), kw.get("dt", 0), kw.get("out", P), None]
     for f, args in ((d, dargs), (g, gargs)):
         assert f(*args(N=40)) == SHAPE                   # N % 16
         assert f(*args(N=0)) == SHAPE
@@ -190,6 +192,7 @@ def test_w4a16_validation(lib):
         assert f(*args(z=0)) == NULL
         assert f(*args(codes=2)) == DTYPE               # neither u4 nor s4
         assert f(*args(codes=-1)) == DTYPE
+        assert f(*args(dt=2)) == DTYPE                  # neither bf16 nor binary16
     assert d(*dargs(w=P + 4)) == ALIGN
     assert g(*gargs(M=-1)) == SHAPE
     assert g(*gargs(x=P + 2)) == ALIGN

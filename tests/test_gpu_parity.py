@@ -508,40 +508,58 @@ def test_sparse24_empty(b):
 
 def _w4a16_dev(inp):
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-    return (to_dev_bf16(inp.x_bits), t(inp.wq4),
-            t(inp.scales.view(np.int16)).view(torch.bfloat16),
-            t(inp.zeros.view(np.int16)).view(torch.bfloat16))
+    dt = torch.float16 if inp.half else torch.bfloat16
+    h = lambda bits: t(bits.view(np.int16)).view(dt)
+    return h(inp.x_bits), t(inp.wq4), h(inp.scales), h(inp.zeros)
 
 
+def _h_bits_to_f64(bits: np.ndarray, half: bool) -> np.ndarray:
+    """16-bit patterns (bf16, or binary16 with half) -> float64 values."""
+    if half:
+        return np.ascontiguousarray(bits).view(np.float16).astype(np.float64)
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _h_ulp(x: np.ndarray, half: bool) -> np.ndarray:
+    """Spacing of the format's values at |x|: bf16 (8 significant bits, binary32 exponents) or
+    binary16 (11 significant bits, subnormal spacing 2^-24)."""
+    if not half:
+        return _bf16_ulp(x)
+    a = np.maximum(np.abs(x), 2.0 ** -14)
+    return np.exp2(np.floor(np.log2(a)) - 10)
+
+
+@pytest.mark.parametrize("half", [False, True])
 @pytest.mark.parametrize("signed", [False, True])
 @pytest.mark.parametrize("N,K,G", [(16, 128, 128), (48, 256, 32), (64, 512, 64), (32, 1024, 256),
                                    (4096, 4096, 128)])
-def test_w4a16_dequant_bit_exact(b, oracle, N, K, G, signed):
-    log(f"w4a16 dequant N={N} K={K} G={G} signed={signed}")
-    inp = make_w4a16(1, N, K, G, seed=N + K + G, signed=signed)
+def test_w4a16_dequant_bit_exact(b, oracle, N, K, G, signed, half):
+    log(f"w4a16 dequant N={N} K={K} G={G} signed={signed} half={half}")
+    inp = make_w4a16(1, N, K, G, seed=N + K + G, signed=signed, half=half)
     _, wq4, s, z = _w4a16_dev(inp)
     got = bf16_bits(b.w4a16_dequant(wq4, s, z, signed=signed))
-    ref = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros, signed=signed)
+    ref = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros, signed=signed, half=half)
     bad = np.argwhere(got != ref)
     assert bad.size == 0, f"{len(bad)} weights differ, first {bad[:4].tolist()}"
 
 
 def _w4a16_case(b, oracle, inp, what, rows=None, signed=False):
-    """w4a16_gemm against the oracle: the exact sum of the bf16 products rounded once, with
-    |gpu - oracle| <= 1 bf16 ulp + K * 2^-24 * sum_k |x w| (fp32 accumulation); on the
-    given rows only (the oracle computes them one by one) when rows is set."""
+    """w4a16_gemm against the oracle: the exact sum of the 16-bit products rounded once, with
+    |gpu - oracle| <= 1 ulp of the format + K * 2^-24 * sum_k |x w| (fp32 accumulation); on
+    the given rows only (the oracle computes them one by one) when rows is set."""
+    half = inp.half
     x, wq4, s, z = _w4a16_dev(inp)
     got = bf16_bits(b.w4a16_gemm(x, wq4, s, z, signed=signed))
-    w = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros, signed=signed)
+    w = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros, signed=signed, half=half)
     x_bits = inp.x_bits if rows is None else inp.x_bits[rows]
     got = got if rows is None else got[rows]
-    ref = oracle.bf16_gemm(x_bits, w)
-    g = bf16_bits_to_f32(got).astype(np.float64)
-    o = bf16_bits_to_f32(ref).astype(np.float64)
-    xa = np.abs(bf16_bits_to_f32(x_bits).astype(np.float64))
-    wa = np.abs(bf16_bits_to_f32(w).astype(np.float64))
+    ref = (oracle.f16_gemm if half else oracle.bf16_gemm)(x_bits, w)
+    g = _h_bits_to_f64(got, half)
+    o = _h_bits_to_f64(ref, half)
+    xa = np.abs(_h_bits_to_f64(x_bits, half))
+    wa = np.abs(_h_bits_to_f64(w, half))
     K = xa.shape[1]
-    bound = _bf16_ulp(np.maximum(np.abs(g), np.abs(o))) + K * 2.0 ** -24 * (xa @ wa.T)
+    bound = _h_ulp(np.maximum(np.abs(g), np.abs(o)), half) + K * 2.0 ** -24 * (xa @ wa.T)
     excess = np.abs(g - o) - bound
     assert (excess <= 0).all(), f"{what}: {int((excess > 0).sum())} outputs outside the bound"
     ulps = ulp_distance(got, ref)
@@ -570,6 +588,25 @@ def test_w4a16_gemm_signed_codes(b, oracle, M, N, K, G):
     log(f"w4a16 gemm s4 M={M} N={N} K={K} G={G}")
     _w4a16_case(b, oracle, make_w4a16(M, N, K, G, seed=M + N + K + 1, signed=True),
                 f"s4 M={M} N={N} K={K}", signed=True)
+
+
+@pytest.mark.parametrize("signed", [False, True])
+@pytest.mark.parametrize("M,N,K,G", [(16, 128, 4096, 128), (33, 32, 1024, 256),
+                                     (130, 272, 1024, 64), (400, 4160, 256, 64),
+                                     (1024, 4112, 256, 64)])
+def test_w4a16_gemm_f16(b, oracle, M, N, K, G, signed):
+    """IEEE binary16 activations, scales, zeros and outputs on each kernel path."""
+    log(f"w4a16 gemm f16 M={M} N={N} K={K} G={G} signed={signed}")
+    _w4a16_case(b, oracle, make_w4a16(M, N, K, G, seed=M + N + K + 2, signed=signed, half=True),
+                f"f16 M={M} N={N} K={K}", signed=signed)
+
+
+@pytest.mark.parametrize("M", [16, 1024])
+def test_w4a16_gemm_f16_workload(b, oracle, M):
+    log(f"w4a16 f16 workload M={M}")
+    rows = None if M <= 64 else _sampled_rows(M, n=24)
+    _w4a16_case(b, oracle, make_w4a16(M, 4096, 4096, 128, seed=0, half=True),
+                f"f16 M={M} N=K=4096", rows)
 
 
 @pytest.mark.parametrize("M", [16, 1024])
