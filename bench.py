@@ -267,18 +267,19 @@ def bench_w4a16(args, torch, np, b, dev):
     w_bytes = N * K // 2 + 2 * 2 * N * (K // G)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    def setup(M):
-        inp = make_w4a16(M, N, K, G, seed=0)
+    def setup(M, signed=False, half=False):
+        inp = make_w4a16(M, N, K, G, seed=0, signed=signed, half=half)
         R = rotation(w_bytes + 2 * M * K + 2 * M * N)
-        x = t(inp.x_bits.view(np.int16)).view(torch.bfloat16)
-        ws = [(t(inp.wq4), t(inp.scales.view(np.int16)).view(torch.bfloat16),
-               t(inp.zeros.view(np.int16)).view(torch.bfloat16)) for _ in range(R)]
-        outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        dt = torch.float16 if half else torch.bfloat16
+        h = lambda bits: t(bits.view(np.int16)).view(dt)
+        x = h(inp.x_bits)
+        ws = [(t(inp.wq4), h(inp.scales), h(inp.zeros)) for _ in range(R)]
+        outs = [torch.empty((M, N), dtype=dt, device=dev) for _ in range(R)]
         return inp, x, ws, outs, R
 
-    def fused_time(M, steps):
-        inp, x, ws, outs, R = setup(M)
-        fn = lambda i: b.w4a16_gemm(x, *ws[i % R], out=outs[i % R])
+    def fused_time(M, steps, signed=False, half=False):
+        inp, x, ws, outs, R = setup(M, signed, half)
+        fn = lambda i: b.w4a16_gemm(x, *ws[i % R], signed=signed, out=outs[i % R])
         for i in range(max(args.warmup, R)):
             fn(i)
         return inp, time_median(fn, steps, torch, R, args.eager), R, x, ws
@@ -299,6 +300,10 @@ def bench_w4a16(args, torch, np, b, dev):
         roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
     roof.update({"traffic": None, "kernel": "w4a16_gemm", "avg_launch_us": round(ms * 1e3, 3)})
+    # the other code and value formats at the same M (signed codes, binary16 values)
+    formats = {}
+    for name, sg, hf in (("s4_bf16", True, False), ("u4_f16", False, True), ("s4_f16", True, True)):
+        formats[name + "_us"] = round(fused_time(M, max(50, args.steps // 4), sg, hf)[1] * 1e3, 3)
 
     sweep = []
     for m in W4A16_M:
@@ -323,6 +328,7 @@ def bench_w4a16(args, torch, np, b, dev):
                    "step": "w4a16_gemm", "seed": 0, "input_sets_rotated": R},
         "roofline": roof,
         "gemm_only": {"us": round(ms * 1e3, 3), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1)},
+        "formats": formats,
         "sweep_n4096_k4096_g128": sweep,
     }
     if not args.no_cpu_baseline:
