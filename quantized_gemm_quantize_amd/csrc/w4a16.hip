@@ -18,6 +18,10 @@
 #include "launch.hpp"
 
 namespace w4a16 {
+
+// Wait until at most n vector-memory operations of this wavefront are
+// outstanding (vmcnt(n); expcnt and lgkmcnt left alone).
+#define W4A16_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 namespace {
 
 using w8a8::kWave;
@@ -392,6 +396,12 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
         __builtin_amdgcn_sched_barrier(0);
         load_codes(min(s + 3, last), into);
         __builtin_amdgcn_sched_barrier(0);
+        // Stage s+1, whose codes compute() dequantizes, has landed once at most
+        // the loads of stages s+2 and s+3 are outstanding. Said explicitly:
+        // the compiler's own wait analysis loses count of one code set across
+        // the unrolled loop and would otherwise drain every load in flight.
+        W4A16_WAIT_VM(2 * NLD);
+        __builtin_amdgcn_sched_barrier(0);  // no use of a loaded value moves above the wait
         compute(xcur, wcur, deq, wnext);
         w8a8::vm_barrier<2 * NLD>();
     };
