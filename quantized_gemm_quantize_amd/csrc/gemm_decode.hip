@@ -4,7 +4,8 @@
 // bound by reading W [N,K] from HBM once (pytorch/ao PR #153 notes that fused
 // dequant GEMMs aimed at compute-bound M > 16 do not serve this memory-bound
 // inference case). Shape of the kernel:
-//  - one workgroup per 16 output channels; its KSPLIT wavefronts split K, so
+//  - one workgroup per 16 output channels; its KSPLIT wavefronts (2, 4 or 8 by
+//    the number of 16-row blocks) split K, so
 //    every wavefront issues all of its 16-byte W loads up front and the whole
 //    weight matrix is in flight at once across the chip;
 //  - v_mfma_i32_16x16x64_i8: lane l holds W row (l % 16) and activation row
@@ -33,9 +34,9 @@
 namespace w8a8 {
 namespace {
 
-constexpr int kUnroll = 8;   // K steps whose loads are issued together
 
-template <int MT, int KSPLIT, bool OUT_I32, bool ADDMM>
+// kSteps: K steps (64 bytes each) whose loads a wavefront issues together.
+template <int MT, int KSPLIT, bool OUT_I32, bool ADDMM, int kSteps>
 __global__ __launch_bounds__(KSPLIT *kWave) void gemm_decode_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ sa, const int8_t *__restrict__ B,
     const float *__restrict__ sb, void *__restrict__ out, int M, int N, int K,
@@ -73,10 +74,10 @@ __global__ __launch_bounds__(KSPLIT *kWave) void gemm_decode_kernel(
     const int s_begin = wave * steps_per_wave;
     const int s_end = min(s_begin + steps_per_wave, total_steps);
     const v4i zero = v4i{};
-    for (int s = s_begin; s < s_end; s += kUnroll) {
-        v4i b[kUnroll], a[MT][kUnroll];
+    for (int s = s_begin; s < s_end; s += kSteps) {
+        v4i b[kSteps], a[MT][kSteps];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kSteps; ++u) {
             const int k = (s + u) * 64;
             const bool ok = (s + u < s_end) && (k + kgrp * 16 < K);
             b[u] = ok ? *reinterpret_cast<const v4i *>(brow + k) : zero;
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(KSPLIT *kWave) void gemm_decode_kernel(
             for (int mb = 0; mb < MT; ++mb) a[mb][u] = ok ? *reinterpret_cast<const v4i *>(arow[mb] + k) : zero;
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < kSteps; ++u)
 #pragma unroll
             for (int mb = 0; mb < MT; ++mb) acc[mb] = mfma_16x16x64(a[mb][u], b[u], acc[mb]);
     }
@@ -274,22 +275,31 @@ hipError_t launch_linear_mt(const uint16_t *x, int M, const int8_t *wq, const fl
     return hipGetLastError();
 }
 
+// Wavefronts per workgroup (the K split) and K steps per load batch, by row
+// blocks. Fewer, longer wavefronts keep the same bytes in flight and are all
+// dispatched sooner (M = 16, K = N = 4096: 2 x 32 runs 6.6 us, 4 x 16 6.8 us,
+// 8 x 8 7.25 us; M = 17: 4 x 16 7.45 us against 7.7 us); more row blocks need
+// the registers for their activations.
+template <int MT> struct DecodeShape { static constexpr int split = 8, steps = 8; };
+template <> struct DecodeShape<1> { static constexpr int split = 2, steps = 32; };
+template <> struct DecodeShape<2> { static constexpr int split = 4, steps = 16; };
+
 template <int MT>
 hipError_t launch_mt(const int8_t *xq, const float *xs, int M, const int8_t *wq, const float *ws,
                      int N, int K, void *out, bool out_i32, hipStream_t stream, const Addmm *am) {
-    constexpr int KSPLIT = 8;
+    constexpr int KSPLIT = DecodeShape<MT>::split, STEPS = DecodeShape<MT>::steps;
     const int total_steps = (K + 63) / 64;
     const int steps_per_wave = (total_steps + KSPLIT - 1) / KSPLIT;
     const dim3 grid((unsigned)(N / 16)), block(KSPLIT * kWave);
     const Addmm a = am ? *am : Addmm{nullptr, 1.0f, 0.0f};
     if (out_i32)
-        gemm_decode_kernel<MT, KSPLIT, true, false>
+        gemm_decode_kernel<MT, KSPLIT, true, false, STEPS>
             <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, steps_per_wave, a);
     else if (am)
-        gemm_decode_kernel<MT, KSPLIT, false, true>
+        gemm_decode_kernel<MT, KSPLIT, false, true, STEPS>
             <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, steps_per_wave, a);
     else
-        gemm_decode_kernel<MT, KSPLIT, false, false>
+        gemm_decode_kernel<MT, KSPLIT, false, false, STEPS>
             <<<grid, block, 0, stream>>>(xq, xs, wq, ws, out, M, N, K, steps_per_wave, a);
     return hipGetLastError();
 }
