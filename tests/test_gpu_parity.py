@@ -138,6 +138,8 @@ GEMM_SHAPES = [
     (1, 16, 16), (16, 128, 256), (5, 48, 80), (17, 64, 4112), (33, 32, 192), (64, 96, 512),
     (65, 144, 160), (130, 272, 400), (257, 256, 384), (300, 528, 272), (520, 1040, 1056),
     (1100, 2064, 272), (129, 16, 16),
+    # M-small shapes with K long enough for the 2- and 4-wavefront splits, ragged K tails
+    (16, 64, 4112), (1, 32, 8208), (32, 48, 4096), (20, 16, 6160),
 ]
 
 
@@ -283,7 +285,7 @@ def _assert_addmm_close(oracle, got, acc, sx, sw, bias, alpha, beta):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (16, 256, 512), (64, 128, 256), (300, 512, 320),
-                                   (129, 1024, 4096)])
+                                   (129, 1024, 4096), (16, 128, 4112), (30, 64, 4096)])
 @pytest.mark.parametrize("alpha,beta,with_bias", [(1.0, 1.0, True), (0.5, -2.0, True),
                                                   (-1.25, 0.0, True), (2.0, 0.0, False)])
 def test_gemm_addmm(b, oracle, M, N, K, alpha, beta, with_bias):
