@@ -98,10 +98,10 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
 // and writing after. Loads are clamped into the input (a chunk past the row
 // repeats the row's last chunk, a row past M repeats row M - 1): they never
 // branch, and what they bring past the row or past M is not stored. Taken for
-// short batches split four wavefronts per row (M < 8192): 2048 x 4096 rows
-// 10.5 -> 10.0 us, 16 rows 4.05 -> 3.62 us; with many rows (one wavefront per
-// row) it measured slower than one workgroup per row group (38400 x 1024:
-// 25.7 -> 28.4 us), so those keep the plain kernel.
+// bf16 rows split over two or four wavefronts: 2048 x 4096 rows 10.5 -> 10.0
+// us, 16 rows 4.05 -> 3.62 us, 16448 x 5120 (two per row) 53.8 -> 51.1 us;
+// with one wavefront per row it measured slower than one workgroup per row
+// group (38400 x 1024: 25.7 -> 28.4 us), so those keep the plain kernel.
 constexpr int kPersistBlocksPerCU = 16;
 
 template <int NCH, int WPR>
@@ -173,7 +173,7 @@ hipError_t launch_wpr(const T *x, int64_t M, int K, int8_t *xq, float *xs, hipSt
     constexpr int kRowsPerBlock = kWavesPerBlock / WPR;
     const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(kThreads);
     const int chunks_per_lane = ((K >> 3) + kWave * WPR - 1) / (kWave * WPR);
-    constexpr bool kPersist = std::is_same<T, uint16_t>::value && WPR == 4;
+    constexpr bool kPersist = std::is_same<T, uint16_t>::value && WPR >= 2;
     const int64_t groups = (M + kRowsPerBlock - 1) / kRowsPerBlock;
     const dim3 pgrid((unsigned)std::min<int64_t>(groups, (int64_t)kPersistBlocksPerCU * device_cu_count()));
     switch (chunks_per_lane) {
