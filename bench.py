@@ -204,7 +204,7 @@ def bench_decode(torch, np, b, dev, steps, warmup, eager=False):
         b.w8a8_quantize_rows(d["x"], xq2, sx2)
         b.w8a8_gemm(xq2, sx2, wqs[i % R], d["sw"], out=out)
 
-    fused = lambda i: b.w8a8_fused_linear(d["x"], wqs[i % R], d["sw"], beta=0.0, out=out)
+    fused = lambda i: b.w8a8_fused_linear(d["x"], wqs[i % R], d["sw"], out=out)
 
     for i in range(warmup):
         step(i)

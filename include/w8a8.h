@@ -39,8 +39,10 @@
  *    launches nothing (pointers sized by M may then be NULL).
  *  - Base pointers must be 16-byte aligned (W8A8_ERR_ALIGN).
  *  - K must be a positive multiple of 16 and at most W8A8_MAX_K, so that
- *    127*127*K < 2^31 and int32 accumulation is exact (pytorch/ao PR #821,
- *    2**31 / 2**14 headroom remark) (W8A8_ERR_SHAPE / W8A8_ERR_K_OVERFLOW).
+ *    128*128*K < 2^31 and int32 accumulation is exact for any int8 operands,
+ *    -128 included (pytorch/ao PR #821, the 2**31 / 2**14 headroom remark:
+ *    2^14 is the largest product of two int8 values) (W8A8_ERR_SHAPE /
+ *    W8A8_ERR_K_OVERFLOW).
  *  - A launch failure returns W8A8_ERR_HIP; w8a8_last_hip_error() then gives
  *    the hipError_t.
  */
@@ -70,8 +72,10 @@ typedef enum {
     W8A8_OUT_I32 = 1   /* out is int32 [M,N]: raw accumulators, for exactness checks */
 } w8a8_out_dtype;
 
-/* Largest K with 127*127*K < 2^31 that is a multiple of 16. */
-#define W8A8_MAX_K 133136
+/* Largest K with 128*128*K < 2^31 that is a multiple of 16: the int32 sum of
+ * K products of int8 values cannot overflow, whatever the caller's codes
+ * (quantize_rows itself never writes -128). */
+#define W8A8_MAX_K 131056
 
 /*
  * Dynamic per-row quantization of bf16 activations.

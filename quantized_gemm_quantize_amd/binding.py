@@ -26,7 +26,7 @@ W8A8_ERR_HIP = -7
 W8A8_ERR_VALUE = -8
 W8A8_OUT_BF16 = 0
 W8A8_OUT_I32 = 1
-W8A8_MAX_K = 133136
+W8A8_MAX_K = 131056
 W8A8_FUSED_MAX_M = 64
 
 _lib = None
@@ -95,6 +95,14 @@ def _check_tensor(t: torch.Tensor, name: str, dtype, ndim: int):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _default_beta(bias, beta):
+    """beta of an addmm call: as given, else 1 with a bias and 0 without (the C ABI
+    rejects a nonzero beta without a bias)."""
+    if beta is None:
+        return 1.0 if bias is not None else 0.0
+    return beta
+
+
 def _call(fn: str, *args):
     st = getattr(load(), fn)(*args)
     if st != W8A8_OK:
@@ -161,10 +169,11 @@ def w8a8_gemm(xq, x_scale, wq, w_scale, out=None, out_dtype="bf16", stream=None)
     return out
 
 
-def w8a8_gemm_addmm(xq, x_scale, wq, w_scale, bias=None, alpha=1.0, beta=1.0, out=None,
+def w8a8_gemm_addmm(xq, x_scale, wq, w_scale, bias=None, alpha=1.0, beta=None, out=None,
                     stream=None):
     """out [M,N] = bf16(alpha * (sum_k xq[m,k] wq[n,k] * x_scale[m] * w_scale[n]) + beta * bias[n]);
-    bias None (allowed with beta == 0) means no bias term."""
+    bias None means no bias term; beta defaults to 1 with a bias and 0 without."""
+    beta = _default_beta(bias, beta)
     _check_tensor(xq, "xq", torch.int8, 2)
     _check_tensor(x_scale, "x_scale", torch.float32, 1)
     _check_tensor(wq, "wq", torch.int8, 2)
@@ -305,11 +314,12 @@ def w8a8_bsr_gemm(xq, x_scale, crow, col, values, w_scale, out=None, out_dtype="
     return out
 
 
-def w8a8_bsr_gemm_addmm(xq, x_scale, crow, col, values, w_scale, bias=None, alpha=1.0, beta=1.0,
+def w8a8_bsr_gemm_addmm(xq, x_scale, crow, col, values, w_scale, bias=None, alpha=1.0, beta=None,
                         out=None, stream=None):
     """Block-sparse W8A8 GEMM with the addmm epilogue (bf16 out):
     out = bf16(alpha * (acc * x_scale[m] * w_scale[n]) + beta * bias[n]); bias None
-    (allowed with beta == 0) means no bias term."""
+    means no bias term; beta defaults to 1 with a bias and 0 without."""
+    beta = _default_beta(bias, beta)
     _check_tensor(xq, "xq", torch.int8, 2)
     _check_tensor(x_scale, "x_scale", torch.float32, 1)
     _check_tensor(crow, "crow", torch.int32, 1)
@@ -333,11 +343,12 @@ def w8a8_bsr_gemm_addmm(xq, x_scale, crow, col, values, w_scale, bias=None, alph
     return out
 
 
-def w8a8_fused_linear(x, wq, w_scale, bias=None, alpha=1.0, beta=1.0, out=None, stream=None):
+def w8a8_fused_linear(x, wq, w_scale, bias=None, alpha=1.0, beta=None, out=None, stream=None):
     """Single-launch quantize + GEMM for x [M,K] bf16 with M <= 64:
     out = bf16(alpha * (acc * s[m] * w_scale[n]) + beta * bias[n]), q and s as
-    w8a8_quantize_rows computes them; bias None (allowed with beta == 0) means
-    no bias term."""
+    w8a8_quantize_rows computes them; bias None means no bias term; beta
+    defaults to 1 with a bias and 0 without."""
+    beta = _default_beta(bias, beta)
     _check_tensor(x, "x", torch.bfloat16, 2)
     _check_tensor(wq, "wq", torch.int8, 2)
     _check_tensor(w_scale, "w_scale", torch.float32, 1)

@@ -48,6 +48,42 @@ __device__ __forceinline__ int xcd_contiguous(int pid, int tiles) {
     return base + idx;
 }
 
+// Dequantization of an int32 accumulator, acc * sa * sb, without an
+// intermediate that overflows or underflows where the result does not: each
+// scale is split once into a significand in [0.5, 1) and a power of two
+// (v_frexp_*), the int32 is multiplied by the two significands (two fp32
+// roundings, no overflow: |acc| < 2^31) and the exponents are applied last
+// with one v_ldexp_f32 (exact unless the result is subnormal or overflows).
+// The result is within 2^-23 (relative) of the exact product, far inside one
+// bf16 ulp (2^-8). A left-to-right (acc * sa) * sb would overflow to inf for
+// rows of magnitude ~1e37 whose exact output is a finite bf16.
+struct SplitScale {
+    float f;  // significand, [0.5, 1), or 0
+    int e;    // power of two
+};
+
+__device__ __forceinline__ SplitScale split_scale(float s) {
+    return SplitScale{__builtin_amdgcn_frexp_mantf(s), __builtin_amdgcn_frexp_expf(s)};
+}
+
+__device__ __forceinline__ float dequant(int acc, SplitScale a, SplitScale b) {
+    return __builtin_amdgcn_ldexpf((float)acc * a.f * b.f, a.e + b.e);
+}
+
+// A scale that is 0 or in [2^-40, 2^40]. When both scales of an output are
+// tame, the plain left-to-right (acc * sa) * sb stays in the fp32 normal
+// range for every int32 acc (|acc * sa| <= 2^71, the product <= 2^111, both
+// >= 2^-80 unless zero), so its three roundings (int32 -> fp32, two products)
+// keep it within 2^-22 of the exact value: the cheaper form applies. Kernels
+// whose epilogue is arithmetic-heavy take it when every scale a wavefront
+// touches is tame (a wave-uniform vote) and the split form otherwise.
+__device__ __forceinline__ bool tame_scale(float s) {
+    const uint32_t u = __float_as_uint(s);
+    return u == 0 || u - 0x2B800000u <= 0x53800000u - 0x2B800000u;
+}
+
+__device__ __forceinline__ bool wave_all(bool p) { return __builtin_amdgcn_ballot_w64(!p) == 0; }
+
 // addmm epilogue of the GEMMs (bf16 output): out[m, n] = bf16(alpha * (acc *
 // sa[m] * sb[n]) + beta * bias[n]); no bias term when bias is null.
 struct Addmm {

@@ -134,8 +134,8 @@ __device__ __forceinline__ void load_stage(const int8_t *__restrict__ at, const 
 // out in two bursts, after the first and the second MFMA (reads r with
 // r % 2 == slot), so they have the rest of the step's MFMAs to land; then
 // one direct-to-LDS load follows each further MFMA (this step's share of the
-// stage loads, steps 0-2). The order is pinned with scheduling barriers: a
-// wavefront issues in order, and a burst of loads would hold the MFMAs.
+// stage loads). The order is pinned with scheduling barriers: a wavefront
+// issues in order, and a burst of loads would hold the MFMAs.
 template <int BM, int CPR, int TM, int TN, int STAGES, int A_LD, int B_LD, bool KTAIL>
 __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
                                                const int8_t *__restrict__ bt,
@@ -147,10 +147,16 @@ __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
                                                v4i (&wb)[2][TN]) {
     constexpr int NLD = A_LD + B_LD;
     constexpr int NMF = TM * TN;        // MFMAs per K step
-    constexpr int NRD = TM + TN;        // fragment reads per K step
     constexpr int KS = CPR / 2;         // K steps per stage
-    constexpr int LPK = (NLD + KS - 2) / (KS - 1);  // loads per K step, steps 0..KS-2
-    constexpr int NSLOT = NMF + 2 > NRD + LPK ? NMF + 2 : NRD + LPK;
+    // With three buffers the stage being loaded is not the next one read, so
+    // its loads may also follow the stage barrier: they are spread over all K
+    // steps, and the barrier waits for all but the LPRE issued before it. With
+    // two, every load of the next stage precedes the barrier.
+    constexpr bool LATE = STAGES == 3;
+    constexpr int LSTEPS = LATE ? KS : KS - 1;
+    constexpr int LPK = (NLD + LSTEPS - 1) / LSTEPS;  // loads per K step
+    constexpr int LPRE = LATE ? ((KS - 1) * LPK < NLD ? (KS - 1) * LPK : NLD) : 0;
+    constexpr int NSLOT = NMF > 2 + LPK ? NMF : 2 + LPK;
     const int j_ahead = s + STAGES - 1;
     const bool ahead = j_ahead < g.nk;  // uniform
     const int k0 = j_ahead * 16 * CPR;
@@ -166,7 +172,7 @@ __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
             // issued in this one may still be in flight), this wavefront's
             // reads of this stage are done; after the barrier both hold for all
             if (ahead)
-                stage_barrier<(STAGES - 2) * NLD>();
+                stage_barrier<LPRE>();
             else
                 stage_barrier<0>();
         }
@@ -181,7 +187,7 @@ __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
             __builtin_amdgcn_sched_barrier(0);
             if (q < 2) {
 #pragma unroll
-                for (int r = 0; r < NRD; ++r) {
+                for (int r = 0; r < TM + TN; ++r) {
                     if (r % 2 != q) continue;
                     if (r < TM)
                         xa[f ^ 1][r] = __builtin_bit_cast(v4i, src_buf[a_frag + r * 32 * CPR + ch]);
@@ -190,7 +196,7 @@ __device__ __forceinline__ void mainloop_stage(const int8_t *__restrict__ at,
                 }
             }
             const int l = kk * LPK + (q - 2);
-            if (kk + 1 < KS && q >= 2 && q < 2 + LPK && l < NLD && ahead) {
+            if (kk < LSTEPS && q >= 2 && q < 2 + LPK && l < NLD && ahead) {
                 uint4 *dst = wr + g.wslot + (l < A_LD ? 256 * l : BM * CPR + 256 * (l - A_LD));
                 const int8_t *src = l < A_LD ? at + g.aoff[l] + k0 : bt + g.boff[l - A_LD] + k0;
                 if (in)
@@ -335,10 +341,16 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_tiled_kernel(
         static_assert(CH == 8 || CH == 16, "the row-chunk permutation needs 8 or 16 chunks per row");
         constexpr int PM = CH - 1;
         uint2 *st8 = reinterpret_cast<uint2 *>(lds) + wave * (WM * WN / 4);
-        // per 4 channels: their scales (and bias) once, then the TM rows
+        // per 4 channels: their scales (and bias) once, then the TM rows. The
+        // plain (acc * sa) * sb when every scale of the wavefront is tame (a
+        // vote per 4 channels), the split form otherwise (see tame_scale)
         float sxv[TM];
+        bool rows_tame = true;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) sxv[i] = sa[min(mw0 + i * 32 + frag_row, M - 1)];
+        for (int i = 0; i < TM; ++i) {
+            sxv[i] = sa[min(mw0 + i * 32 + frag_row, M - 1)];
+            rows_tame = rows_tame && tame_scale(sxv[i]);
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -347,16 +359,27 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_tiled_kernel(
                 const float4 w = *reinterpret_cast<const float4 *>(sb + n);
                 float4 bv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 if (ADDMM && am.bias) bv = *reinterpret_cast<const float4 *>(am.bias + n);
+                const bool cheap = wave_all(rows_tame && tame_scale(w.x) && tame_scale(w.y) &&
+                                            tame_scale(w.z) && tame_scale(w.w));
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
                     const int ml = i * 32 + frag_row;
                     const v16i &a = acc[i][j];
-                    const uint32_t lo =
-                        pack_bf16x2(addmm<ADDMM>((float)a[4 * g] * sxv[i] * w.x, am, bv.x),
-                                    addmm<ADDMM>((float)a[4 * g + 1] * sxv[i] * w.y, am, bv.y));
-                    const uint32_t hi =
-                        pack_bf16x2(addmm<ADDMM>((float)a[4 * g + 2] * sxv[i] * w.z, am, bv.z),
-                                    addmm<ADDMM>((float)a[4 * g + 3] * sxv[i] * w.w, am, bv.w));
+                    float v[4];
+                    if (cheap) {
+                        v[0] = (float)a[4 * g] * sxv[i] * w.x;
+                        v[1] = (float)a[4 * g + 1] * sxv[i] * w.y;
+                        v[2] = (float)a[4 * g + 2] * sxv[i] * w.z;
+                        v[3] = (float)a[4 * g + 3] * sxv[i] * w.w;
+                    } else {
+                        const SplitScale x = split_scale(sxv[i]);
+                        v[0] = dequant(a[4 * g], x, split_scale(w.x));
+                        v[1] = dequant(a[4 * g + 1], x, split_scale(w.y));
+                        v[2] = dequant(a[4 * g + 2], x, split_scale(w.z));
+                        v[3] = dequant(a[4 * g + 3], x, split_scale(w.w));
+                    }
+                    const uint32_t lo = pack_bf16x2(addmm<ADDMM>(v[0], am, bv.x), addmm<ADDMM>(v[1], am, bv.y));
+                    const uint32_t hi = pack_bf16x2(addmm<ADDMM>(v[2], am, bv.z), addmm<ADDMM>(v[3], am, bv.w));
                     const int chunk = (j * 4 + g) ^ (ml & PM);
                     st8[(ml * CH + chunk) * 2 + half] = make_uint2(lo, hi);
                 }

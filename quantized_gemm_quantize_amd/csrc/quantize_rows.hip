@@ -156,14 +156,16 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_persistent(
     // two register sets, alternating (a copy between them would wait for the
     // load); every wavefront of the workgroup runs the same iterations, so the
     // barriers inside process() are reached by all
+    // (the guards are uniform: a workgroup never fetches a group it will not
+    // process)
     uint4 ua[NCH], ub[NCH];
     int64_t g = blockIdx.x;
     load_raw(g, ua);
     for (; g < groups; g += 2 * G) {
-        load_raw(g + G, ub);
+        if (g + G < groups) load_raw(g + G, ub);
         process(g, ua, 0);
         if (g + G >= groups) break;
-        load_raw(g + 2 * G, ua);
+        if (g + 2 * G < groups) load_raw(g + 2 * G, ua);
         process(g + G, ub, 1);
     }
 }

@@ -165,7 +165,8 @@ __global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_kernel(
         if constexpr (OUT_I32)
             static_cast<int32_t *>(out)[(int64_t)m * N + n] = sum;
         else
-            static_cast<__bf16 *>(out)[(int64_t)m * N + n] = (__bf16)((float)sum * sx[m] * sw[n]);
+            static_cast<__bf16 *>(out)[(int64_t)m * N + n] =
+                (__bf16)dequant(sum, split_scale(sx[m]), split_scale(sw[n]));
     }
 }
 
@@ -395,22 +396,40 @@ __global__ __launch_bounds__(kTThreads, 1) void sparse24_tiled_kernel(
         constexpr int CH = kTWN / 8;
         uint2 *st8 = reinterpret_cast<uint2 *>(lds) + wave * (kTWM * kTWN / 4);
         float sxv[kTTM];
+        bool rows_tame = true;
 #pragma unroll
-        for (int i = 0; i < kTTM; ++i) sxv[i] = sx[min(mw0 + i * 32 + frag_row, M - 1)];
+        for (int i = 0; i < kTTM; ++i) {
+            sxv[i] = sx[min(mw0 + i * 32 + frag_row, M - 1)];
+            rows_tame = rows_tame && tame_scale(sxv[i]);
+        }
 #pragma unroll
         for (int j = 0; j < kTTN; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = min(nw0 + j * 32 + 8 * g + 4 * half, N - 4);
                 const float4 w = *reinterpret_cast<const float4 *>(sw + n);
+                // the plain product when the wavefront's scales are all tame
+                const bool cheap = wave_all(rows_tame && tame_scale(w.x) && tame_scale(w.y) &&
+                                            tame_scale(w.z) && tame_scale(w.w));
 #pragma unroll
                 for (int i = 0; i < kTTM; ++i) {
                     const int ml = i * 32 + frag_row;
                     const v16i &a = acc[i][j];
-                    const uint32_t lo = pack_bf16x2((float)a[4 * g] * sxv[i] * w.x,
-                                                    (float)a[4 * g + 1] * sxv[i] * w.y);
-                    const uint32_t hi = pack_bf16x2((float)a[4 * g + 2] * sxv[i] * w.z,
-                                                    (float)a[4 * g + 3] * sxv[i] * w.w);
+                    float v[4];
+                    if (cheap) {
+                        v[0] = (float)a[4 * g] * sxv[i] * w.x;
+                        v[1] = (float)a[4 * g + 1] * sxv[i] * w.y;
+                        v[2] = (float)a[4 * g + 2] * sxv[i] * w.z;
+                        v[3] = (float)a[4 * g + 3] * sxv[i] * w.w;
+                    } else {
+                        const SplitScale x = split_scale(sxv[i]);
+                        v[0] = dequant(a[4 * g], x, split_scale(w.x));
+                        v[1] = dequant(a[4 * g + 1], x, split_scale(w.y));
+                        v[2] = dequant(a[4 * g + 2], x, split_scale(w.z));
+                        v[3] = dequant(a[4 * g + 3], x, split_scale(w.w));
+                    }
+                    const uint32_t lo = pack_bf16x2(v[0], v[1]);
+                    const uint32_t hi = pack_bf16x2(v[2], v[3]);
                     st8[(ml * CH + ((j * 4 + g) ^ (ml & 7))) * 2 + half] = make_uint2(lo, hi);
                 }
             }

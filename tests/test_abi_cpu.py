@@ -52,8 +52,8 @@ def test_header_constants_match_binding():
     assert re.search(rf"W4A16_CODES_S4\s*=\s*{binding.W4A16_CODES_S4}\b", text)
     assert re.search(rf"W4A16_BF16\s*=\s*{binding.W4A16_BF16}\b", text)
     assert re.search(rf"W4A16_F16\s*=\s*{binding.W4A16_F16}\b", text)
-    assert 127 * 127 * binding.W8A8_MAX_K < 2 ** 31
-    assert 127 * 127 * (binding.W8A8_MAX_K + 16) >= 2 ** 31
+    assert 128 * 128 * binding.W8A8_MAX_K < 2 ** 31
+    assert 128 * 128 * (binding.W8A8_MAX_K + 16) >= 2 ** 31
     for name in ("W8A8_ERR_NULL", "W8A8_ERR_SHAPE", "W8A8_ERR_ALIGN", "W8A8_ERR_K_OVERFLOW",
                  "W8A8_ERR_BLOCKSIZE", "W8A8_ERR_DTYPE", "W8A8_ERR_HIP", "W8A8_ERR_VALUE"):
         m = re.search(rf"{name}\s*=\s*(-?\d+)", text)

@@ -4,10 +4,10 @@ The library launches on the stream it is given and never synchronizes, so a
 whole layer (quantize, the dense GEMM on both paths, the addmm epilogues, the
 single-launch linear, block-sparse, 2:4 and W4A16 products) can run on a side
 stream or be captured into a HIP graph and replayed. Bar: bit-identical
-outputs to the eager calls on the default stream, on every replay, with eager
-work (output clearing, other launches) between the replays; the eager outputs
-themselves are checked against the oracle on one product so the comparison is
-anchored.
+outputs to the eager calls on the default stream, on each of ten eager runs and
+ten graph replays, with eager work (output clearing, other launches) between
+the replays; the eager outputs themselves are checked against the oracle on one
+product so the comparison is anchored.
 """
 import numpy as np
 import pytest
@@ -20,6 +20,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 M, N, K = 320, 384, 512   # tiled paths with ragged M; N, K multiples of 128
 MD = 16                   # the M-small paths
+KL = 4096                 # the M-small path with both operands through LDS
+REPEATS = 10
 
 
 @pytest.fixture(scope="module")
@@ -48,6 +50,9 @@ def layer(b):
     t["xd"] = _bf16(dense.x_bits[:MD])
     t["wq"], t["sw"] = b.w8a8_quantize_rows_f32(_dev(dense.w))
     t["bias"] = _dev((np.random.default_rng(22).standard_normal(N) * 0.5).astype(np.float32))
+    long_k = make_linear(MD, N, KL, seed=26)
+    t["xl"] = _bf16(long_k.x_bits)
+    t["wql"], t["swl"] = b.w8a8_quantize_rows_f32(_dev(long_k.w))
     blk = make_linear(M, N, K, seed=23, bs=64, zero_frac=0.6)
     wqb, t["swb"] = b.w8a8_quantize_rows_f32(_dev(blk.w))
     crow, col, values = bsr_from_dense(wqb.cpu().numpy(), blk.block_mask, 64)
@@ -65,7 +70,10 @@ def layer(b):
     t["sx"] = torch.empty((M,), dtype=torch.float32, device=DEV)
     t["xqd"] = torch.empty((MD, K), dtype=torch.int8, device=DEV)
     t["sxd"] = torch.empty((MD,), dtype=torch.float32, device=DEV)
+    t["xql"] = torch.empty((MD, KL), dtype=torch.int8, device=DEV)
+    t["sxl"] = torch.empty((MD,), dtype=torch.float32, device=DEV)
     for name, rows in (("gemm", M), ("addmm", M), ("dec", MD), ("dec_addmm", MD), ("fused", MD),
+                       ("decl", MD), ("decl_addmm", MD),
                        ("bsr", M), ("bsr_addmm", M), ("s24", M), ("s24d", MD), ("w4", M),
                        ("w4d", MD)):
         t["out_" + name] = torch.empty((rows, N), dtype=torch.bfloat16, device=DEV)
@@ -73,8 +81,9 @@ def layer(b):
     return t
 
 
-OUTPUTS = ["xq", "sx", "xqd", "sxd", "out_gemm", "out_addmm", "out_dec", "out_dec_addmm",
-           "out_fused", "out_bsr", "out_bsr_addmm", "out_s24", "out_s24d", "out_w4", "out_w4d"]
+OUTPUTS = ["xq", "sx", "xqd", "sxd", "xql", "sxl", "out_gemm", "out_addmm", "out_dec",
+           "out_dec_addmm", "out_decl", "out_decl_addmm", "out_fused", "out_bsr", "out_bsr_addmm",
+           "out_s24", "out_s24d", "out_w4", "out_w4d"]
 
 
 def run_layer(b, t, stream=None):
@@ -89,6 +98,10 @@ def run_layer(b, t, stream=None):
                       out=t["out_dec_addmm"], stream=stream)
     b.w8a8_fused_linear(t["xd"], t["wq"], t["sw"], bias=t["bias"], alpha=1.0, beta=1.0,
                         out=t["out_fused"], stream=stream)
+    b.w8a8_quantize_rows(t["xl"], t["xql"], t["sxl"], stream=stream)
+    b.w8a8_gemm(t["xql"], t["sxl"], t["wql"], t["swl"], out=t["out_decl"], stream=stream)
+    b.w8a8_gemm_addmm(t["xql"], t["sxl"], t["wql"], t["swl"], bias=t["bias"], alpha=0.5,
+                      beta=-0.75, out=t["out_decl_addmm"], stream=stream)
     b.w8a8_bsr_gemm(t["xq"], t["sx"], t["crow"], t["col"], t["values"], t["swb"],
                     out=t["out_bsr"], stream=stream)
     b.w8a8_bsr_gemm_addmm(t["xq"], t["sx"], t["crow"], t["col"], t["values"], t["swb"],
@@ -155,8 +168,18 @@ def test_side_stream(b, layer, eager_ref):
         assert_same(layer, eager_ref, f"side stream ({'argument' if explicit else 'current'})")
 
 
+def test_eager_repeats(b, layer, eager_ref):
+    """Ten more eager runs of every entry point, each after clearing the outputs: bit-identical
+    every time (no order-dependent reductions, no stale state between calls)."""
+    for rep in range(REPEATS):
+        clear_outputs(layer)
+        run_layer(b, layer)
+        torch.cuda.synchronize()
+        assert_same(layer, eager_ref, f"eager run {rep}")
+
+
 def test_graph_replays(b, layer, eager_ref):
-    """The layer captured into one HIP graph: three replays, each after eager clearing of the
+    """The layer captured into one HIP graph: ten replays, each after eager clearing of the
     outputs and an unrelated eager launch, each bit-identical to the eager run."""
     warm = torch.cuda.Stream()
     warm.wait_stream(torch.cuda.current_stream())
@@ -169,7 +192,7 @@ def test_graph_replays(b, layer, eager_ref):
         run_layer(b, layer)
     torch.cuda.synchronize()
     other = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-    for rep in range(3):
+    for rep in range(REPEATS):
         clear_outputs(layer)
         b.w8a8_gemm(layer["xq"], layer["sx"], layer["wq"], layer["sw"], out=other)  # eager work
         torch.cuda.synchronize()

@@ -176,6 +176,19 @@ def test_int32_headroom_bound(oracle):
         oracle.gemm_i32(big, neg)
 
 
+def test_int32_headroom_bound_full_int8_range(oracle):
+    # -128 * -128 = 2^14 per product (the page's 2^31 / 2^14 remark): 2^14 K < 2^31 up to
+    # K = 131071, the largest multiple of 16 being 131056, the library's K limit
+    K = 131056
+    m128 = np.full((1, K), -128, np.int8)
+    acc = oracle.gemm_i32(m128, m128)
+    assert int(acc[0, 0]) == 2 ** 14 * K and 2 ** 14 * K < 2 ** 31 <= 2 ** 14 * (K + 16)
+    K2 = K + 16
+    big = np.full((1, K2), -128, np.int8)
+    with pytest.raises(OverflowError):
+        oracle.gemm_i32(big, big)
+
+
 # --- bf16 rounding and the epilogue ----------------------------------------
 
 def test_bf16_rounding_matches_torch_cast(oracle):
