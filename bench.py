@@ -21,6 +21,18 @@ The line also carries:
                (quantize + GEMM) and the single-launch w8a8_fused_linear, both
                priced at the layer's bytes (X bf16 + Wq + sw + out).
 
+  peaks        reference rates measured on the same GPU in the same run
+               (libpeaks.so): the int8 MFMA issue rate of back-to-back
+               v_mfma_i32_32x32x32_i8 with the shader clock it ran at
+               (s_memtime against the 100 MHz reference), HBM streaming read
+               and write rates over 1 GiB, and the time to stream-read 16.8 MB
+               (the M=16 weight matrix) with the buffers rotated past the
+               Infinity Cache. roofline.frac_measured is the kernel's rate
+               against these (for HBM-bound kernels: the time its read and
+               write bytes take at the measured rates, over its time);
+  clocks       amd-smi's gfx and memory clocks sampled while the step's HIP
+               graph replays for about two seconds, and at idle.
+
 Inputs are resident in HBM before the timed region; input sets are rotated
 (copies at distinct addresses, more than twice the Infinity Cache in total).
 Launches are captured into HIP graphs and replayed, so the timing is the GPU's
@@ -64,6 +76,10 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch every timed call directly instead of replaying HIP graphs "
                          "(for profilers that count per dispatch)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the on-device reference rates (libpeaks.so) and exit")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the reference rates and the clock sampling")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy five times (the "
                          "reference for scaling HBM byte counters) and exit")
@@ -187,6 +203,131 @@ def cpu_baseline(name: str, np):
                       f"quantize + exact int GEMM + float64 epilogue"
                       + (" (2:4 weight decompressed inside the timed region)" if sparse24 else "")
                       + f", {t:.2f} s wall"}
+
+
+MFMA_RECORD = os.path.join(ROOT, "profiles", "gemm_tiled_prefill_mfma.json")
+
+
+def measure_peaks(torch, eager=False):
+    """Reference rates on this GPU, in this run (see the module docstring)."""
+    import ctypes
+    from quantized_gemm_quantize_amd.build import PEAKS_LIB
+    if not os.path.exists(PEAKS_LIB):
+        raise RuntimeError(f"{PEAKS_LIB} is not built: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(PEAKS_LIB)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.peaks_mfma_i8.argtypes = [i32, i32, p, p, p]
+    lib.peaks_read.argtypes = [p, i64, i32, p, p]
+    lib.peaks_write.argtypes = [p, i64, i32, p]
+    for f in (lib.peaks_mfma_i8, lib.peaks_read, lib.peaks_write):
+        f.restype = i32
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = lambda: torch.cuda.current_stream().cuda_stream
+
+    def call(rc):
+        if rc != 0:
+            raise RuntimeError(f"peaks launch failed ({rc})")
+
+    wgs, iters = 2 * cus, 2000
+    sink = torch.zeros(4 * cus * 256, dtype=torch.int32, device=dev)
+    clk = torch.zeros(2, dtype=torch.int64, device=dev)
+    mf = lambda i: call(lib.peaks_mfma_i8(wgs, iters, sink.data_ptr(), clk.data_ptr(), stream()))
+    mf(0)
+    ms = time_median(mf, 20, torch, 1, eager)
+    c = clk.cpu().tolist()
+    mfma_tops = wgs * 4 * iters * 8 * 65536 / (ms * 1e-3) / 1e12
+    shader_mhz = c[0] / (c[1] / 100e6) / 1e6 if c[1] else None
+
+    nbytes = 1 << 30
+    big = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    call(lib.peaks_write(big.data_ptr(), nbytes, 8 * cus, stream()))
+    rd = lambda i: call(lib.peaks_read(big.data_ptr(), nbytes, 8 * cus, sink.data_ptr(), stream()))
+    wr = lambda i: call(lib.peaks_write(big.data_ptr(), nbytes, 8 * cus, stream()))
+    read_gbs = nbytes / (time_median(rd, 5, torch, 1, eager) * 1e-3) / 1e9
+    write_gbs = nbytes / (time_median(wr, 5, torch, 1, eager) * 1e-3) / 1e9
+    del big
+    # a decode-sized read: the 4096 x 4096 int8 weight, buffers rotated past the MALL
+    small = 4096 * 4096
+    R = rotation(small)
+    bufs = [torch.empty(small, dtype=torch.uint8, device=dev) for _ in range(R)]
+    for t in bufs:
+        call(lib.peaks_write(t.data_ptr(), small, 8 * cus, stream()))
+    rs = lambda i: call(lib.peaks_read(bufs[i % R].data_ptr(), small, 4 * cus, sink.data_ptr(),
+                                       stream()))
+    read_small_us = time_median(rs, 20 * R, torch, R, eager) * 1e3
+    torch.cuda.synchronize()
+    return {"mfma_int8_TOPs": round(mfma_tops, 1), "mfma_loop_shader_MHz": round(shader_mhz, 1),
+            "hbm_read_GBps": round(read_gbs, 1), "hbm_write_GBps": round(write_gbs, 1),
+            "read_16_8MB_us": round(read_small_us, 3),
+            "read_16_8MB_GBps": round(small / (read_small_us * 1e-6) / 1e9, 1),
+            "method": "libpeaks.so: 8 independent v_mfma_i32_32x32x32_i8 chains per wavefront, "
+                      f"{wgs} workgroups of 4 wavefronts; 16-byte loads / streaming stores over "
+                      "1 GiB; 16.8 MB reads over rotated buffers; HIP graph replays, median of 5"}
+
+
+def amd_smi_clocks():
+    """gfx (mean over the XCDs) and memory clocks from one `amd-smi metric -c --json`, or
+    None where the tool is missing or fails."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        data = json.loads(r.stdout)
+        clock = data["gpu_data"][0]["clock"] if isinstance(data, dict) else data[0]["clock"]
+        gfx = [v["clk"]["value"] for k, v in clock.items() if k.startswith("gfx_")
+               and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        mem = [v["clk"]["value"] for k, v in clock.items() if k.startswith("mem_")
+               and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        return {"gfx_MHz": round(sum(gfx) / len(gfx), 1) if gfx else None,
+                "mem_MHz": mem[0] if mem else None}
+    except Exception:
+        return None
+
+
+def clocks_under_load(fn, torch, period, seconds=2.0):
+    """amd-smi samples while the HIP graph of `fn` (one period of rotated calls) replays back
+    to back for about `seconds`; and one sample at idle before."""
+    import threading
+    idle = amd_smi_clocks()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(period):
+            fn(i)
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            c = amd_smi_clocks()
+            if c is None:
+                return
+            samples.append(c)
+    th = threading.Thread(target=poll)
+    torch.cuda.synchronize()
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            g.replay()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    gfx = [c["gfx_MHz"] for c in samples if c.get("gfx_MHz")]
+    return {"idle": idle, "under_load_samples": len(samples),
+            "under_load_gfx_MHz": sorted(gfx), "under_load_mem_MHz":
+            samples[-1]["mem_MHz"] if samples else None}
+
+
+def mfma_record():
+    """The committed rocprofv3 MFMA-counter record of the prefill GEMM, when taken on the
+    current kernel source."""
+    if not os.path.exists(MFMA_RECORD):
+        return None
+    rec = json.load(open(MFMA_RECORD))
+    if rec.get("source_hash") != source_hash(GEMM_SOURCES):
+        return None
+    return {k: rec[k] for k in ("mfma_busy_frac", "mfma_busy_cycles", "gui_active_cycles",
+                                "mops_i8", "kernel") if k in rec}
 
 
 def bench_decode(torch, np, b, dev, steps, warmup, eager=False):
@@ -356,6 +497,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 5}), flush=True)
         return
 
+    if args.peaks:
+        print(json.dumps({"peaks": measure_peaks(torch, args.eager)}), flush=True)
+        return
     from quantized_gemm_quantize_amd import binding as b
     b.load()
     dev = torch.device("cuda:0")
@@ -478,6 +622,19 @@ def main():
         roof = {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS,
                 "unit": "TOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4)}
     roof["traffic"] = traffic
+    peaks = clocks = None
+    if not args.no_peaks:
+        peaks = measure_peaks(torch, args.eager)
+        if roof["bound"] == "mfma":
+            roof["frac_measured"] = round(gemm_tops / peaks["mfma_int8_TOPs"], 4)
+            roof["peak_measured"] = peaks["mfma_int8_TOPs"]
+        else:
+            rbytes = M * K + 4 * M + w_bytes + 4 * N
+            t_ideal = rbytes / (peaks["hbm_read_GBps"] * 1e9) + 2 * M * N / (peaks["hbm_write_GBps"] * 1e9)
+            roof["frac_measured"] = round(t_ideal / (ms_gemm * 1e-3), 4)
+        clocks = clocks_under_load(step, torch, R)
+    if roof["bound"] == "mfma" and name == "prefill_outliers":
+        roof["mfma_counters"] = mfma_record()
     kernel = "w8a8_bsr_gemm" if bsr else "w8a8_sparse24_gemm" if sp24 else "w8a8_gemm"
     roof["kernel"] = kernel
     roof["avg_launch_us"] = round(ms_gemm * 1e3, 3)
@@ -518,6 +675,13 @@ def main():
         line["bsr_addmm"] = bsr_addmm
     if not args.no_decode and name == "prefill_outliers":
         line["decode_m16"] = bench_decode(torch, np, b, dev, args.steps, args.warmup, args.eager)
+        if peaks is not None:
+            dm = line["decode_m16"]
+            t_floor = peaks["read_16_8MB_us"]
+            dm["vs_measured_read_floor"] = round(t_floor / dm["gemm_us"], 4)
+    if peaks is not None:
+        line["peaks"] = peaks
+        line["clocks"] = clocks
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(name, np)
     print(json.dumps(line), flush=True)

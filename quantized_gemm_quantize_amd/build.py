@@ -15,6 +15,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libw8a8.so")
+# on-device reference rates for the benchmark (not part of the library's ABI)
+PEAKS_LIB = os.path.join(HERE, "libpeaks.so")
+PEAKS_SOURCE = "peaks.hip"
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["quantize_rows.hip", "gemm_tiled.hip", "gemm_decode.hip", "bsr_gemm.hip", "sparse24.hip",
            "w4a16.hip", "w8a8_abi.hip"]
@@ -41,17 +44,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build_library(jobs: int = 8) -> str:
-    """Compile every source and link libw8a8.so (always rebuilds)."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build_library(jobs: int = 8) -> str:
+    """Compile every source and link libw8a8.so, and the benchmark's reference-rate kernels
+    into libpeaks.so (always rebuilds)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [PEAKS_SOURCE]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PEAKS_LIB)
     return LIB
 
 

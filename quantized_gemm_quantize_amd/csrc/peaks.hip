@@ -1,0 +1,99 @@
+// On-device reference rates for the benchmark (not part of the W8A8 path):
+// the int8 MFMA issue rate and the HBM streaming read and write rates that the
+// kernels' roofline fractions are also quoted against, measured on the same
+// GPU in the same run as the kernels, since MI355X's clock under int8 MFMA
+// load is power-limited below the nominal peak's 2.4 GHz.
+//
+// peaks_mfma_i8: each wavefront runs `iters` rounds of 8 independent
+//   v_mfma_i32_32x32x32_i8 on register operands (8 accumulators, so the issue
+//   never waits on a result); 65536 ops each. The operands are varied per lane
+//   so the multipliers toggle as under real data.
+// peaks_read: every thread reads 16-byte chunks, grid-stride, and folds them
+//   into one word per thread (written once, so the loads cannot be dropped).
+// peaks_write: every thread writes 16-byte chunks, grid-stride, with streaming
+//   stores (as the GEMM epilogues do).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void mfma_loop(int iters, int *sink, uint64_t *clk) {
+    const int lane = threadIdx.x & 63;
+    // the shader clock over the loop: s_memtime counts core clocks, s_memrealtime
+    // the constant 100 MHz reference (workgroup 0, first wavefront)
+    const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    v4i a = {lane * 0x01030507 + 0x11, lane * 0x0f0d0b09 + 0x2b, lane ^ 0x5a5a5a5a, ~lane * 0x01010101};
+    v4i b = {lane * 0x07050301 + 0x3d, lane ^ 0x3c3c3c3c, lane * 0x090b0d0f + 0x47, lane * 0x13171d1f};
+    v16i acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = v16i{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[i], 0, 0, 0);
+        a = a ^ (v4i){it, it, it, it};  // keeps the operands varied, off the MFMA's critical path
+    }
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s ^= acc[i][e];
+    if (s == 0x7fffffff) sink[blockIdx.x] = s;  // practically never: keeps the loop alive
+    const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        clk[0] = c1 - c0;
+        clk[1] = r1 - r0;
+    }
+}
+
+__global__ __launch_bounds__(256) void read_loop(const uint4 *__restrict__ p, int64_t n16,
+                                                 uint32_t *__restrict__ sink) {
+    uint32_t s = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        const uint4 v = p[i];
+        s ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (s == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void write_loop(uint4 *__restrict__ p, int64_t n16, uint32_t v) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        typedef int v4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store((v4){(int)v, (int)i, (int)v, (int)i}, reinterpret_cast<v4 *>(p + i));
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+// workgroups: launched workgroups of 256 threads; the ops are
+// workgroups * 4 * iters * 8 * 65536. sink: at least `workgroups` ints.
+// clk[0], clk[1]: core clocks and 100 MHz reference ticks over workgroup 0's
+// loop (their ratio is the shader clock under int8 MFMA load).
+int peaks_mfma_i8(int workgroups, int iters, int *sink, uint64_t *clk, void *stream) {
+    if (workgroups <= 0 || iters <= 0 || !sink || !clk) return -1;
+    mfma_loop<<<workgroups, 256, 0, static_cast<hipStream_t>(stream)>>>(iters, sink, clk);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+// bytes: a multiple of 16; sink: at least workgroups * 256 words.
+int peaks_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink, void *stream) {
+    if (bytes <= 0 || bytes % 16 || workgroups <= 0 || !buf || !sink) return -1;
+    read_loop<<<workgroups, 256, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const uint4 *>(buf), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int peaks_write(void *buf, int64_t bytes, int workgroups, void *stream) {
+    if (bytes <= 0 || bytes % 16 || workgroups <= 0 || !buf) return -1;
+    write_loop<<<workgroups, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<uint4 *>(buf),
+                                                                       bytes / 16, 0x5bd1e995u);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+}  // extern "C"
