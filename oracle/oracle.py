@@ -30,14 +30,31 @@ def build_oracle() -> str:
     return _LIB
 
 
+# A sanitizer build (AddressSanitizer + UndefinedBehaviorSanitizer) of the same
+# source, for the CPU tests that run the pins under it.
+SAN_CFLAGS = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+              "-fno-omit-frame-pointer", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+              "-fPIC", "-shared", "-Wall", "-Wextra", "-Werror"]
+
+
+def build_oracle_sanitized(path: str) -> str:
+    """Compile the oracle with AddressSanitizer and UndefinedBehaviorSanitizer into `path`
+    (loaded in place of liboracle.so when W8A8_ORACLE_LIB names it, with gcc's sanitizer
+    runtimes preloaded)."""
+    subprocess.run(["gcc", *SAN_CFLAGS, "-o", path, _SRC, "-lm"], check=True)
+    return path
+
+
 def load_oracle():
-    """Load liboracle.so, building it first only if it is absent."""
+    """Load liboracle.so (or the library W8A8_ORACLE_LIB names), building liboracle.so
+    first only if it is absent."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
+    path = os.environ.get("W8A8_ORACLE_LIB", _LIB)
+    if path == _LIB and not os.path.exists(_LIB):
         build_oracle()
-    lib = ctypes.CDLL(_LIB)
+    lib = ctypes.CDLL(path)
     p = ctypes.c_void_p
     i64 = ctypes.c_int64
     lib.oracle_quantize_rows_bf16.argtypes = [p, i64, i64, p, p]

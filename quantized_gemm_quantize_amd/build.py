@@ -35,9 +35,15 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for the CPU tests: only the host
+# half of each translation unit is instrumented (the gfx950 code objects are unchanged).
+HOST_SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def _compile(src: str, out_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -62,6 +68,17 @@ def build_library(jobs: int = 8) -> str:
     _link(objs[:-1], LIB)
     _link(objs[-1:], PEAKS_LIB)
     return LIB
+
+
+def build_host_sanitized(lib: str, jobs: int = 8) -> str:
+    """libw8a8.so with the host code under AddressSanitizer + UndefinedBehaviorSanitizer, for
+    the CPU tests of the C ABI (loaded with clang's AddressSanitizer runtime preloaded)."""
+    out_dir = os.path.join(os.path.dirname(lib), "objs")
+    os.makedirs(out_dir, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, out_dir, HOST_SAN_FLAGS), SOURCES))
+    _link(objs, lib)
+    return lib
 
 
 if __name__ == "__main__":

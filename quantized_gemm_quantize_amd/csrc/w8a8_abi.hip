@@ -11,6 +11,7 @@
 
 #include <climits>
 #include <cmath>
+#include <cstring>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -20,6 +21,17 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// A C caller may pass any int for an enum parameter, but in C++ reading an
+// enum object whose value lies outside its enumerators' range is undefined:
+// selectors are read as the int they are, then validated.
+template <typename E>
+int selector(const E *e) {
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+    int v;
+    std::memcpy(&v, e, sizeof v);
+    return v;
+}
 
 w8a8_status hip_status(hipError_t e) {
     if (e == hipSuccess) return W8A8_OK;
@@ -89,7 +101,8 @@ w8a8_status w8a8_gemm(const int8_t *xq, const float *x_scale, int64_t M, const i
                       w8a8_out_dtype out_dtype, void *stream) {
     if (M < 0 || N <= 0 || N % 16 != 0 || too_big(M, N)) return W8A8_ERR_SHAPE;
     if (w8a8_status s = check_k(K)) return s;
-    if (out_dtype != W8A8_OUT_BF16 && out_dtype != W8A8_OUT_I32) return W8A8_ERR_DTYPE;
+    const int od = selector(&out_dtype);
+    if (od != W8A8_OUT_BF16 && od != W8A8_OUT_I32) return W8A8_ERR_DTYPE;
     if ((M + 127) / 128 > INT_MAX / ((N + 127) / 128)) return W8A8_ERR_SHAPE;  // grid.x
     if (M == 0) return W8A8_OK;
     if (!xq || !x_scale || !wq || !w_scale || !out) return W8A8_ERR_NULL;
@@ -97,7 +110,7 @@ w8a8_status w8a8_gemm(const int8_t *xq, const float *x_scale, int64_t M, const i
         misaligned(out))
         return W8A8_ERR_ALIGN;
     return hip_status(w8a8::launch_gemm(xq, x_scale, (int)M, wq, w_scale, (int)N, (int)K, out,
-                                        out_dtype == W8A8_OUT_I32,
+                                        od == W8A8_OUT_I32,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -147,7 +160,8 @@ w8a8_status w8a8_bsr_gemm(const int8_t *xq, const float *x_scale, int64_t M, int
         return W8A8_ERR_SHAPE;
     if (w8a8_status s = check_k(K)) return s;
     if (nnzb > (N / bs) * (K / bs)) return W8A8_ERR_SHAPE;
-    if (out_dtype != W8A8_OUT_BF16 && out_dtype != W8A8_OUT_I32) return W8A8_ERR_DTYPE;
+    const int od = selector(&out_dtype);
+    if (od != W8A8_OUT_BF16 && od != W8A8_OUT_I32) return W8A8_ERR_DTYPE;
     if ((M + 127) / 128 > INT_MAX / (N / bs)) return W8A8_ERR_SHAPE;  // grid.x
     if (M == 0) return W8A8_OK;
     if (!xq || !x_scale || !crow || !w_scale || !out) return W8A8_ERR_NULL;
@@ -157,7 +171,7 @@ w8a8_status w8a8_bsr_gemm(const int8_t *xq, const float *x_scale, int64_t M, int
         return W8A8_ERR_ALIGN;
     return hip_status(w8a8::launch_bsr_gemm(xq, x_scale, (int)M, (int)K, crow, col, values,
                                             (int)nnzb, w_scale, (int)N, out,
-                                            out_dtype == W8A8_OUT_I32,
+                                            od == W8A8_OUT_I32,
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -204,7 +218,8 @@ w8a8_status w8a8_sparse24_gemm(const int8_t *xq, const float *x_scale, int64_t M
                                void *stream) {
     if (M < 0 || N <= 0 || N % 16 != 0 || K % 128 != 0 || too_big(M, N)) return W8A8_ERR_SHAPE;
     if (w8a8_status s = check_k(K)) return s;
-    if (out_dtype != W8A8_OUT_BF16 && out_dtype != W8A8_OUT_I32) return W8A8_ERR_DTYPE;
+    const int od = selector(&out_dtype);
+    if (od != W8A8_OUT_BF16 && od != W8A8_OUT_I32) return W8A8_ERR_DTYPE;
     if ((M + 127) / 128 > INT_MAX / ((N + 255) / 256)) return W8A8_ERR_SHAPE;  // grid.x
     if (M == 0) return W8A8_OK;
     if (!xq || !x_scale || !values || !meta || !w_scale || !out) return W8A8_ERR_NULL;
@@ -212,7 +227,7 @@ w8a8_status w8a8_sparse24_gemm(const int8_t *xq, const float *x_scale, int64_t M
         misaligned(w_scale) || misaligned(out))
         return W8A8_ERR_ALIGN;
     return hip_status(w8a8::launch_sparse24_gemm(xq, x_scale, (int)M, values, meta, w_scale,
-                                                 (int)N, (int)K, out, out_dtype == W8A8_OUT_I32,
+                                                 (int)N, (int)K, out, od == W8A8_OUT_I32,
                                                  static_cast<hipStream_t>(stream)));
 }
 
@@ -230,15 +245,16 @@ w8a8_status w4a16_dequant(const uint8_t *wq4, const void *scales, const void *ze
                           int64_t K, int64_t group_size, w4a16_codes codes, w4a16_dtype dtype,
                           void *w, void *stream) {
     if (w8a8_status s = w4a16_shape(N, K, group_size)) return s;
-    if (codes != W4A16_CODES_U4 && codes != W4A16_CODES_S4) return W8A8_ERR_DTYPE;
-    if (dtype != W4A16_BF16 && dtype != W4A16_F16) return W8A8_ERR_DTYPE;
+    const int cs = selector(&codes), dt = selector(&dtype);
+    if (cs != W4A16_CODES_U4 && cs != W4A16_CODES_S4) return W8A8_ERR_DTYPE;
+    if (dt != W4A16_BF16 && dt != W4A16_F16) return W8A8_ERR_DTYPE;
     if (!wq4 || !scales || !zeros || !w) return W8A8_ERR_NULL;
     if (misaligned(wq4) || misaligned(w) || misaligned2(scales) || misaligned2(zeros))
         return W8A8_ERR_ALIGN;
     return hip_status(w4a16::launch_dequant(wq4, static_cast<const uint16_t *>(scales),
                                             static_cast<const uint16_t *>(zeros), (int)N, (int)K,
-                                            (int)group_size, codes == W4A16_CODES_S4,
-                                            dtype == W4A16_F16, static_cast<uint16_t *>(w),
+                                            (int)group_size, cs == W4A16_CODES_S4,
+                                            dt == W4A16_F16, static_cast<uint16_t *>(w),
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -247,8 +263,9 @@ w8a8_status w4a16_gemm(const void *x, int64_t M, const uint8_t *wq4, const void 
                        w4a16_codes codes, w4a16_dtype dtype, void *out, void *stream) {
     if (M < 0 || M > INT_MAX / 2) return W8A8_ERR_SHAPE;
     if (w8a8_status s = w4a16_shape(N, K, group_size)) return s;
-    if (codes != W4A16_CODES_U4 && codes != W4A16_CODES_S4) return W8A8_ERR_DTYPE;
-    if (dtype != W4A16_BF16 && dtype != W4A16_F16) return W8A8_ERR_DTYPE;
+    const int cs = selector(&codes), dt = selector(&dtype);
+    if (cs != W4A16_CODES_U4 && cs != W4A16_CODES_S4) return W8A8_ERR_DTYPE;
+    if (dt != W4A16_BF16 && dt != W4A16_F16) return W8A8_ERR_DTYPE;
     if ((M + 63) / 64 > INT_MAX / ((N + 63) / 64)) return W8A8_ERR_SHAPE;  // grid.x
     if (M == 0) return W8A8_OK;
     if (!x || !wq4 || !scales || !zeros || !out) return W8A8_ERR_NULL;
@@ -258,8 +275,8 @@ w8a8_status w4a16_gemm(const void *x, int64_t M, const uint8_t *wq4, const void 
     return hip_status(w4a16::launch_gemm(static_cast<const uint16_t *>(x), (int)M, wq4,
                                          static_cast<const uint16_t *>(scales),
                                          static_cast<const uint16_t *>(zeros), (int)N, (int)K,
-                                         (int)group_size, codes == W4A16_CODES_S4,
-                                         dtype == W4A16_F16, static_cast<uint16_t *>(out),
+                                         (int)group_size, cs == W4A16_CODES_S4,
+                                         dt == W4A16_F16, static_cast<uint16_t *>(out),
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -269,7 +286,7 @@ const char *w8a8_status_string(int status) {
         case W8A8_ERR_NULL: return "a required pointer is NULL";
         case W8A8_ERR_SHAPE: return "a size is out of range or not a required multiple";
         case W8A8_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
-        case W8A8_ERR_K_OVERFLOW: return "K exceeds the int32-safe bound (127*127*K < 2^31)";
+        case W8A8_ERR_K_OVERFLOW: return "K exceeds the int32-safe bound (128*128*K < 2^31)";
         case W8A8_ERR_BLOCKSIZE: return "BSR block size must be 64";
         case W8A8_ERR_DTYPE: return "unknown output dtype";
         case W8A8_ERR_HIP: return "HIP launch error (see w8a8_last_hip_error)";
