@@ -31,9 +31,10 @@
  *  - All array pointers are DEVICE pointers owned by the caller; the library
  *    allocates nothing, keeps no state between calls (except the thread-local
  *    last HIP error) and is reentrant.
- *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
- *    and the call returns without synchronizing. Outputs are valid once the
- *    stream reaches that point.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void *, so the
+ *    header needs no HIP include; NULL = the default stream) and the call
+ *    returns without synchronizing. Outputs are valid once the stream reaches
+ *    that point.
  *  - Arguments are validated on the host before any HIP call; a failed check
  *    returns its code and launches nothing. M == 0 is a valid empty call that
  *    launches nothing (pointers sized by M may then be NULL).
@@ -78,7 +79,11 @@ typedef enum {
 #define W8A8_MAX_K 131056
 
 /*
- * Dynamic per-row quantization of bf16 activations.
+ * Dynamic per-row quantization of bf16 activations: the scale is the row
+ * absmax over 127 in binary32 (Paddle sparse_fc PR #41770, spmm_plugin.cu
+ * weight-scale hunk), computed per token at run time with no calibration
+ * (pytorch/ao PR #821, "int8 dynamicquant"), and values are clamped before
+ * the cast (vLLM csrc/quantization log, FP8 clamp commit).
  *   x_bf16  [M,K] bf16, row-major (read)
  *   xq      [M,K] int8, row-major (written): clamp(rint(fl32(x / s)), -127, 127)
  *   x_scale [M]   fp32 (written): s = fl32(max_k |x[m,k]| / 127); s = 0 and
@@ -100,7 +105,12 @@ w8a8_status w8a8_quantize_rows_f32(const float *x, int64_t M, int64_t K, int8_t 
                                    float *x_scale, void *stream);
 
 /*
- * Dense W8A8 GEMM with the fused dequant epilogue.
+ * Dense W8A8 GEMM with the fused dequant epilogue: int8 x int8 products summed
+ * in int32 (pytorch/ao PR #821, "triton dot accumulator uses int32"), scaled by
+ * the row and channel scales and rounded to bf16 inside the kernel so the
+ * int32 matrix never reaches memory (same PR: the fused-dequant paragraph and
+ * the i8i8 -> bf16 change), both operands K-contiguous (triton issue #634,
+ * layout answer).
  *   xq      [M,K] int8 row-major, x_scale [M] fp32   (from w8a8_quantize_rows)
  *   wq      [N,K] int8, K-contiguous (one row per output channel)
  *   w_scale [N]   fp32 per output channel
@@ -160,7 +170,11 @@ w8a8_status w8a8_fused_linear(const void *x_bf16, int64_t M, int64_t K, const in
 /*
  * Block-sparse (BSR) W8A8 GEMM with the fused dequant epilogue: only stored
  * weight blocks are read and multiplied; output channels of block rows with
- * no stored block are written as +0.
+ * no stored block are written as +0. The weight is given as raw crow / col /
+ * values arrays of 64x64 blocks (pytorch/ao PR #821: the custom-op paragraph
+ * and the bsr_dense_addmm warning for 64x64 blocks), and the output is the
+ * [M,N] layer output itself, with no transposed copy (same PR, the
+ * ".t().contiguous()" suggestions).
  *   xq, x_scale as for w8a8_gemm ([M,K] int8, [M] fp32)
  *   crow    [N/bs + 1] int32: block row r owns blocks crow[r] .. crow[r+1]-1,
  *           crow[0] = 0, non-decreasing, crow[N/bs] = nnzb
@@ -169,7 +183,10 @@ w8a8_status w8a8_fused_linear(const void *x_bf16, int64_t M, int64_t K, const in
  *           (each block row K-contiguous, like the dense [N,K] weight)
  *   w_scale [N] fp32 per output channel, out [M,N] as for w8a8_gemm.
  * bs must be 64; N and K positive multiples of 64; nnzb >= 0 (col and values
- * may be NULL when nnzb == 0). Malformed index arrays (out-of-range entries,
+ * may be NULL when nnzb == 0). The bf16 epilogue is within one bf16 ulp for
+ * every row scale and for channel scales that are 0 or in [2^-125, 2^97]
+ * (w8a8_quantize_rows_f32 gives such scales for weight rows whose absmax lies
+ * in [2^-118, 2^104]); outside that range an output may lose that bound. Malformed index arrays (out-of-range entries,
  * decreasing crow) give unspecified output values, but the kernel clamps every
  * index so it never reads outside the given arrays.
  * Errors: NULL, SHAPE, K_OVERFLOW, BLOCKSIZE, ALIGN, DTYPE, HIP.

@@ -255,9 +255,6 @@ __device__ __forceinline__ void store_zero_rows(const Args &a, int m0, int br, i
 //
 // ADDMM: out = bf16(alpha * (acc * sa * sb) + beta * bias[n]). EMPTY (addmm
 // only): a block row without stored blocks, acc = 0 and no ring buffer.
-// The product is formed without an overflowing intermediate (split_scale):
-// this kernel is bound by its output writes, and its consumers have no
-// registers to spare for a second, cheaper form.
 template <typename OutT, bool ADDMM, bool EMPTY>
 __device__ __forceinline__ void store_tile(const Args &a, const uint4 *__restrict__ buf,
                                            uint4 *__restrict__ stg, const v16i (&acc)[kTM][2],
@@ -291,7 +288,9 @@ __device__ __forceinline__ void store_tile(const Args &a, const uint4 *__restric
         const int i = rg * kSR / 32;  // MFMA row tile of this pass
         // with 16-row passes, half of the lanes hold the pass's rows
         const bool mine = kSR == 32 || (frag_row >> 4) == (rg & 1);
-        const SplitScale sxs = split_scale(kI32 || EMPTY ? 0.0f : sa_l[kRowsPerMath * w + 32 * i + frag_row]);
+        // the row scale as significand and power of two (see the products below)
+        const SplitScale sx =
+            split_scale(kI32 || EMPTY ? 0.0f : sa_l[kRowsPerMath * w + 32 * i + frag_row]);
 #pragma unroll
         for (int h = 0; h < kPieces; ++h) {
             if (mine) {
@@ -313,20 +312,20 @@ __device__ __forceinline__ void store_tile(const Args &a, const uint4 *__restric
                             const int cb = 32 * jt + 8 * g;
                             const float4 bv = half ? make_float4(ub[cb + 4], ub[cb + 5], ub[cb + 6], ub[cb + 7])
                                                    : make_float4(ub[cb], ub[cb + 1], ub[cb + 2], ub[cb + 3]);
+                            // acc * sa * sb as ldexp((acc * f) * sb, e) with
+                            // sa = f * 2^e, f in [0.5, 1): no intermediate
+                            // overflows or underflows for any row scale, nor
+                            // for channel scales in [2^-125, 2^97]
                             float v[4];
                             const float sc[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                v[e] = dequant(acc[i][jt][4 * g + e], sxs, split_scale(sc[e]));
+                                v[e] = __builtin_amdgcn_ldexpf((float)acc[i][jt][4 * g + e] * sx.f * sc[e], sx.e);
                             const uint32_t lo = pack_bf16x2(addmm<ADDMM>(v[0], a.am, bv.x),
                                                             addmm<ADDMM>(v[1], a.am, bv.y));
                             const uint32_t hi = pack_bf16x2(addmm<ADDMM>(v[2], a.am, bv.z),
                                                             addmm<ADDMM>(v[3], a.am, bv.w));
                             *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
-                            // one channel group at a time: the next group's
-                            // scale reads are not hoisted above this one
-                            // (their registers would not fit)
-                            asm volatile("" ::: "memory");
                         }
                     }
                 }
