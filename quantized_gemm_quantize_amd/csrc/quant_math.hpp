@@ -51,16 +51,33 @@ __device__ __forceinline__ void widen8(uint4 u, float v[8]) {
     }
 }
 
+// 16 bytes with the nontemporal (streaming) hint, for inputs read exactly
+// once: the hint keeps them from displacing reused lines in the caches. On
+// the row quantization (bf16 in, codes out) it measured 9.0 -> 7.3 us at
+// 2048 x 4096 and 52 -> 46 us at 16448 x 5120.
+__device__ __forceinline__ uint4 load16_stream(const void *p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p)));
+}
+
+template <bool STREAM>
+__device__ __forceinline__ uint4 load16(const void *p) {
+    if constexpr (STREAM) return load16_stream(p);
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
 // 8 consecutive inputs -> float, and their absmax folded into `amax`.
+// STREAM: the input is read only this once (see load16_stream).
+template <bool STREAM>
 __device__ __forceinline__ void load8(const uint16_t *p, float v[8], uint32_t &amax) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint4 u = load16<STREAM>(p);
     widen8(u, v);
     absmax8(u, amax);
 }
 
+template <bool STREAM>
 __device__ __forceinline__ void load8(const float *p, float v[8], uint32_t &amax) {
-    const float4 a = reinterpret_cast<const float4 *>(p)[0];
-    const float4 b = reinterpret_cast<const float4 *>(p)[1];
+    const float4 a = __builtin_bit_cast(float4, load16<STREAM>(p));
+    const float4 b = __builtin_bit_cast(float4, load16<STREAM>(p + 4));
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     float m = __uint_as_float(amax);
@@ -105,24 +122,26 @@ __device__ __forceinline__ float branch_local(float s) {
     return s;
 }
 
-// 8 values -> 8 int8 codes (two packed words)
+// 8 values -> 8 int8 codes (two packed words). The fallback is branched per
+// element: element e takes the division only when some lane of the wavefront
+// has its element e near a tie (about 64 / 8000 of the time), instead of all
+// eight elements whenever any of them is (about 8 x 64 / 8000): 2048 rows of
+// 4096 N(0, 2) values quantize in 7.7 us instead of 9.0 us.
 __device__ __forceinline__ uint2 quantize8(const float v[8], const RowScale &rs) {
     uint32_t b[8];
     if (rs.fast) {
-        bool near_tie = false;
+        bool near_tie[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float t = v[e] * rs.r;
             const float m = t + kMagic;
             const float k = m - kMagic;  // rint(t), exact
-            near_tie |= __builtin_fabsf(t - k) >= kTieGuard;
+            near_tie[e] = __builtin_fabsf(t - k) >= kTieGuard;
             b[e] = __float_as_uint(m);
         }
-        if (near_tie) {
-            const float s = branch_local(rs.s);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) b[e] = quantize_div(v[e], s);
-        }
+        for (int e = 0; e < 8; ++e)
+            if (near_tie[e]) b[e] = quantize_div(v[e], branch_local(rs.s));
     } else if (rs.s != 0.0f) {  // subnormal scale: 1 / s would overflow
         const float s = branch_local(rs.s);
 #pragma unroll

@@ -60,10 +60,11 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int ch = first + c * stride;
-            if (live && ch < nch) load8(xr + ch * 8, v[c], amax);
+            if (live && ch < nch) load8<true>(xr + ch * 8, v[c], amax);
         }
     } else {
-        for (int ch = first; live && ch < nch; ch += stride) load8(xr + ch * 8, v[0], amax);
+        // read twice: the second pass should find the row in L2
+        for (int ch = first; live && ch < nch; ch += stride) load8<false>(xr + ch * 8, v[0], amax);
     }
     amax = wave_max(amax);
     if constexpr (WPR > 1) {
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
     } else {
         for (int ch = first; ch < nch; ch += stride) {
             uint32_t unused = 0;
-            load8(xr + ch * 8, v[0], unused);
+            load8<false>(xr + ch * 8, v[0], unused);
             *reinterpret_cast<uint2 *>(qr + ch * 8) = quantize8(v[0], rs);
         }
     }
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
 // group (38400 x 1024: 25.7 -> 28.4 us), so those keep the plain kernel.
 constexpr int kPersistBlocksPerCU = 16;
 
-template <int NCH, int WPR>
+template <int NCH, int WPR, bool PIPE>
 __global__ __launch_bounds__(kThreads) void quantize_rows_persistent(
     const uint16_t *__restrict__ x, int64_t M, int K, int8_t *__restrict__ xq,
     float *__restrict__ xs) {
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_persistent(
         const uint16_t *xr = x + row * K;
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
-            u[c] = *reinterpret_cast<const uint4 *>(xr + 8 * min(first + c * stride, nch - 1));
+            u[c] = load16_stream(xr + 8 * min(first + c * stride, nch - 1));
     };
     auto process = [&](int64_t g, const uint4 (&u)[NCH], int parity) {
         const int64_t row = g * kRowsPerBlock + wave / WPR;
@@ -158,8 +159,16 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_persistent(
     // barriers inside process() are reached by all
     // (the guards are uniform: a workgroup never fetches a group it will not
     // process)
-    uint4 ua[NCH], ub[NCH];
     int64_t g = blockIdx.x;
+    if constexpr (!PIPE) {
+        // one row group per workgroup (G >= groups): a single register set, so
+        // the kernel stays within 64 VGPRs and every wavefront is resident
+        uint4 ua[NCH];
+        load_raw(g, ua);
+        process(g, ua, 0);
+        return;
+    }
+    uint4 ua[NCH], ub[NCH];
     load_raw(g, ua);
     for (; g < groups; g += 2 * G) {
         if (g + G < groups) load_raw(g + G, ub);
@@ -181,10 +190,14 @@ hipError_t launch_wpr(const T *x, int64_t M, int K, int8_t *xq, float *xs, hipSt
     switch (chunks_per_lane) {
 #define W8A8_Q_CASE(n)                                                                       \
     case n:                                                                                  \
-        if constexpr (kPersist)                                                              \
-            quantize_rows_persistent<n, WPR><<<pgrid, block, 0, stream>>>(                   \
-                reinterpret_cast<const uint16_t *>(x), M, K, xq, xs);                        \
-        else                                                                                 \
+        if constexpr (kPersist) {                                                            \
+            if (groups <= (int64_t)pgrid.x)                                                  \
+                quantize_rows_persistent<n, WPR, false><<<pgrid, block, 0, stream>>>(        \
+                    reinterpret_cast<const uint16_t *>(x), M, K, xq, xs);                    \
+            else                                                                             \
+                quantize_rows_persistent<n, WPR, true><<<pgrid, block, 0, stream>>>(         \
+                    reinterpret_cast<const uint16_t *>(x), M, K, xq, xs);                    \
+        } else                                                                               \
             quantize_rows_kernel<T, n, WPR><<<grid, block, 0, stream>>>(x, M, K, xq, xs);     \
         break;
         W8A8_Q_CASE(1)
