@@ -124,6 +124,19 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// 16-byte load with the nontemporal (streaming) hint, for data read exactly
+// once (the row quantization's input, the M-small kernels' weights): the hint
+// keeps it from displacing reused lines (activations, codes) in the caches.
+// Measured: row quantization of 2048 x 4096 bf16 9.0 -> 7.3 us; the M = 16
+// weight-streaming GEMM (K = N = 4096) 5.86 -> 5.54 us.
+__device__ __forceinline__ uint4 load16_stream(const void *p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p)));
+}
+
+// The cache-policy operand of global_load_lds (direct-to-LDS) that sets the
+// same nontemporal bit.
+constexpr int kLdsLoadStream = 2;
+
 // 16-byte streaming (nontemporal) store.
 __device__ __forceinline__ void store16_nt(void *p, uint4 v) {
     __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), reinterpret_cast<v4i *>(p));

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(KSPLIT *kWave) void gemm_decode_kernel(
         for (int u = 0; u < kSteps; ++u) {
             const int k = (s + u) * 64;
             const bool ok = (s + u < s_end) && (k + kgrp * 16 < K);
-            b[u] = ok ? *reinterpret_cast<const v4i *>(brow + k) : zero;
+            b[u] = ok ? __builtin_bit_cast(v4i, load16_stream(brow + k)) : zero;
 #pragma unroll
             for (int mb = 0; mb < MT; ++mb) a[mb][u] = ok ? *reinterpret_cast<const v4i *>(arow[mb] + k) : zero;
         }
@@ -202,7 +202,8 @@ __global__ __launch_bounds__(WAVES *kWave) void gemm_decode_lds_kernel(
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 __builtin_amdgcn_global_load_lds((global_void *)(wrow[h] + min(kp + cb[h], K - 16)),
-                                                 (lds_void *)(wr + (2 * p + h) * kWave), 16, 0, 0);
+                                                 (lds_void *)(wr + (2 * p + h) * kWave), 16, 0,
+                                                 kLdsLoadStream);
         }
 #pragma unroll
         for (int p = 0; p < kPairs; ++p) {
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(kLinSplit *kWave) void linear_decode_kernel(
                     xr[mb][u][h] = *reinterpret_cast<const v4i *>(xrow[mb] + k_off(s + u) + 8 * h);
         __builtin_amdgcn_sched_barrier(0);  // activations first, then weights
 #pragma unroll
-        for (int u = 0; u < U; ++u) b[u] = *reinterpret_cast<const v4i *>(brow + k_off(s + u));
+        for (int u = 0; u < U; ++u) b[u] = __builtin_bit_cast(v4i, load16_stream(brow + k_off(s + u)));
         __builtin_amdgcn_sched_barrier(0);  // all issued before anything waits on them
     };
 

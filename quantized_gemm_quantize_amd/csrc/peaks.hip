@@ -8,8 +8,10 @@
 //   v_mfma_i32_32x32x32_i8 on register operands (8 accumulators, so the issue
 //   never waits on a result); 65536 ops each. The operands are varied per lane
 //   so the multipliers toggle as under real data.
-// peaks_read: every thread reads 16-byte chunks, grid-stride, and folds them
-//   into one word per thread (written once, so the loads cannot be dropped).
+// peaks_read: every thread reads 16-byte chunks, grid-stride, with the
+//   nontemporal hint (as the kernels that read their weights once do), and
+//   folds them into one word per thread (written once, so the loads cannot be
+//   dropped).
 // peaks_write: every thread writes 16-byte chunks, grid-stride, with streaming
 //   stores (as the GEMM epilogues do).
 #include <hip/hip_runtime.h>
@@ -53,8 +55,8 @@ __global__ __launch_bounds__(256) void read_loop(const uint4 *__restrict__ p, in
     uint32_t s = 0;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
-        const uint4 v = p[i];
-        s ^= v.x ^ v.y ^ v.z ^ v.w;
+        const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p + i));
+        s ^= (uint32_t)(v.x ^ v.y ^ v.z ^ v.w);
     }
     if (s == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }

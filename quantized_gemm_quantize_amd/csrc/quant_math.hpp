@@ -51,14 +51,7 @@ __device__ __forceinline__ void widen8(uint4 u, float v[8]) {
     }
 }
 
-// 16 bytes with the nontemporal (streaming) hint, for inputs read exactly
-// once: the hint keeps them from displacing reused lines in the caches. On
-// the row quantization (bf16 in, codes out) it measured 9.0 -> 7.3 us at
-// 2048 x 4096 and 52 -> 46 us at 16448 x 5120.
-__device__ __forceinline__ uint4 load16_stream(const void *p) {
-    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p)));
-}
-
+// 16 bytes, with the streaming hint (load16_stream) when STREAM.
 template <bool STREAM>
 __device__ __forceinline__ uint4 load16(const void *p) {
     if constexpr (STREAM) return load16_stream(p);

@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_kernel(
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int blk = min(s + u, nblk - 1);
-            const v4i av = *reinterpret_cast<const v4i *>(vrow + blk * vstride);
+            const v4i av = __builtin_bit_cast(v4i, load16_stream(vrow + blk * vstride));
             a[u] = s + u < s_end ? av : v4i{};
             idx[u] = (int)mrow[blk * mstride];
 #pragma unroll

@@ -28,6 +28,7 @@ using w8a8::kWave;
 using w8a8::pack_bf16x2;
 using w8a8::bf16_lo;
 using w8a8::bf16_hi;
+using w8a8::load16_stream;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_kernel(
 #pragma unroll
     for (int mb = 0; mb < MT; ++mb) acc[mb] = v4f{};
     for (int c = c_begin; c < c_end; ++c) {
-        const uint4 codes = *reinterpret_cast<const uint4 *>(wrow + 64 * c);
+        const uint4 codes = load16_stream(wrow + 64 * c);
         const int g = (128 * c + 32 * q) / G;
         const float s = h_to_float<F16>(srow[g]), z = h_to_float<F16>(zrow[g]);
         uint4 xv[MT][4];
