@@ -10,7 +10,7 @@
 // fills the chip); every lane moves 16 input bytes per load, the absmax is
 // reduced across lanes with shuffles and across the row's wavefronts through
 // LDS, and rows of up to NCH*64*8*WPR elements stay in registers so the input
-// is read once.
+// is read once (with the streaming hint, as nothing reads it again).
 //
 // The element arithmetic (exact division on multiplies, rounding, the byte)
 // is in quant_math.hpp.
@@ -92,17 +92,20 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
     if (sub == 0 && lane == 0) xs[row] = rs.s;
 }
 
-// Persistent variant for bf16 rows held in registers: workgroup b runs through
-// the row groups b, b + G, b + 2G, ... (G = gridDim.x) and issues the loads of
-// the next group before it reduces, quantizes and stores the current one, so
-// its stores overlap its next loads instead of all workgroups reading first
-// and writing after. Loads are clamped into the input (a chunk past the row
-// repeats the row's last chunk, a row past M repeats row M - 1): they never
-// branch, and what they bring past the row or past M is not stored. Taken for
-// bf16 rows split over two or four wavefronts: 2048 x 4096 rows 10.5 -> 10.0
-// us, 16 rows 4.05 -> 3.62 us, 16448 x 5120 (two per row) 53.8 -> 51.1 us;
-// with one wavefront per row it measured slower than one workgroup per row
-// group (38400 x 1024: 25.7 -> 28.4 us), so those keep the plain kernel.
+// Persistent variant for bf16 rows held in registers, taken for rows split
+// over two or four wavefronts. With more row groups than workgroups (PIPE),
+// workgroup b runs through the row groups b, b + G, b + 2G, ... (G =
+// gridDim.x) and issues the loads of the next group before it reduces,
+// quantizes and stores the current one, so its stores overlap its next loads
+// (16448 x 5120, two wavefronts per row: 53.8 -> 51.1 us against one
+// workgroup per row group). When every workgroup owns exactly one row group
+// (!PIPE: 2048 x 4096, 16 x 4096) it holds one register set, 44 VGPRs instead
+// of 80, so all its wavefronts are resident at once (2048 x 4096: 7.70 ->
+// 7.37 us). Loads are clamped into the input (a chunk past the row repeats the
+// row's last chunk, a row past M repeats row M - 1): they never branch, and
+// what they bring past the row or past M is not stored. With one wavefront
+// per row the pipelined form measured slower than one workgroup per row group
+// (38400 x 1024: 25.7 -> 28.4 us), so those keep the plain kernel.
 constexpr int kPersistBlocksPerCU = 16;
 
 template <int NCH, int WPR, bool PIPE>
