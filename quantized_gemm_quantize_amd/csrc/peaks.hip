@@ -61,6 +61,25 @@ __global__ __launch_bounds__(256) void read_loop(const uint4 *__restrict__ p, in
     if (s == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// A [rows, 4096] byte matrix read the way the M-small GEMM reads its weight:
+// workgroup b takes rows 16b .. 16b+15, its wavefront w the 1 KB column slice
+// [1024 w, +1024), and every lane issues all 16 of its 16-byte loads (8 rows x
+// 128 bytes per instruction) before using any of them.
+__global__ __launch_bounds__(256) void read_rows(const int8_t *__restrict__ p, uint32_t *__restrict__ sink) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int8_t *base = p + (int64_t)blockIdx.x * 16 * 4096 + 1024 * wave + 16 * (lane & 7);
+    v4i v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        v[q] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(
+            base + (int64_t)(8 * (q & 1) + (lane >> 3)) * 4096 + 128 * (q >> 1)));
+    v4i a = v[0];
+#pragma unroll
+    for (int q = 1; q < 16; ++q) a ^= v[q];
+    const uint32_t s = (uint32_t)(a.x ^ a.y ^ a.z ^ a.w);
+    if (s == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 __global__ __launch_bounds__(256) void write_loop(uint4 *__restrict__ p, int64_t n16, uint32_t v) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
@@ -88,6 +107,15 @@ int peaks_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink, v
     if (bytes <= 0 || bytes % 16 || workgroups <= 0 || !buf || !sink) return -1;
     read_loop<<<workgroups, 256, 0, static_cast<hipStream_t>(stream)>>>(
         static_cast<const uint4 *>(buf), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+// rows: a positive multiple of 16 (rows of 4096 bytes); sink: at least
+// rows / 16 * 256 words.
+int peaks_read_rows(const void *buf, int rows, uint32_t *sink, void *stream) {
+    if (rows <= 0 || rows % 16 || !buf || !sink) return -1;
+    read_rows<<<rows / 16, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const int8_t *>(buf),
+                                                                         sink);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
