@@ -17,6 +17,10 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libw8a8.so")
 # on-device reference rates for the benchmark (not part of the library's ABI)
 PEAKS_LIB = os.path.join(HERE, "libpeaks.so")
+# debug build: every kernel fills its LDS with a fixed pattern before use (W8A8_LDS_POISON);
+# the GPU tests require its outputs to be bit-identical to the normal build's
+POISON_LIB = os.path.join(HERE, "libw8a8_ldspoison.so")
+POISON_FLAGS = ["-DW8A8_LDS_POISON"]
 PEAKS_SOURCE = "peaks.hip"
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["quantize_rows.hip", "gemm_tiled.hip", "gemm_decode.hip", "bsr_gemm.hip", "sparse24.hip",
@@ -60,13 +64,19 @@ def _link(objs, lib):
 
 
 def build_library(jobs: int = 8) -> str:
-    """Compile every source and link libw8a8.so, and the benchmark's reference-rate kernels
-    into libpeaks.so (always rebuilds)."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES) + 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES + [PEAKS_SOURCE]))
-    _link(objs[:-1], LIB)
-    _link(objs[-1:], PEAKS_LIB)
+    """Compile every source and link libw8a8.so, its LDS-poisoned debug twin
+    libw8a8_ldspoison.so, and the benchmark's reference-rate kernels into libpeaks.so
+    (always rebuilds)."""
+    poison_dir = os.path.join(BUILD_DIR, "ldspoison")
+    os.makedirs(poison_dir, exist_ok=True)
+    jobs_list = [(s, BUILD_DIR, ()) for s in SOURCES + [PEAKS_SOURCE]]
+    jobs_list += [(s, poison_dir, POISON_FLAGS) for s in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs_list))
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:n + 1], PEAKS_LIB)
+    _link(objs[n + 1:], POISON_LIB)
     return LIB
 
 

@@ -419,6 +419,9 @@ __global__ __launch_bounds__(kThreads, 4) void bsr_gemm_kernel(Args a, int slabs
     using OutT = typename std::conditional<OUT_I32, int32_t, __bf16>::type;
     __shared__ uint4 lds[kLdsSlots];
     __shared__ int2 meta[kSegTiles];  // stored-block range of each tile of the segment
+    lds_poison(lds);
+    lds_poison(meta);
+    lds_poison_done();
     // the wavefront index is uniform: saying so makes the role branch below a
     // scalar branch with two separate paths
     const int lane = threadIdx.x & (kWave - 1);

@@ -42,6 +42,8 @@ __global__ __launch_bounds__(KSPLIT *kWave) void gemm_decode_kernel(
     const float *__restrict__ sb, void *__restrict__ out, int M, int N, int K,
     int steps_per_wave, Addmm am) {
     __shared__ int red[KSPLIT][MT][4][kWave];
+    lds_poison(red);
+    lds_poison_done();
 
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int n0 = blockIdx.x * 16;
@@ -162,6 +164,9 @@ __global__ __launch_bounds__(WAVES *kWave) void gemm_decode_lds_kernel(
     constexpr int kRegion = kPairs * 2 * kWave;  // 16-byte slots per operand per wavefront
     __shared__ uint4 lds[WAVES * 2 * kRegion];
     __shared__ v4i red[WAVES][kWave];
+    lds_poison(lds);
+    lds_poison(red);
+    lds_poison_done();
 
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int n0 = blockIdx.x * 16;
@@ -257,6 +262,10 @@ __global__ __launch_bounds__(kLinSplit *kWave) void linear_decode_kernel(
     __shared__ int red[kLinSplit][MT][4][kWave];
     __shared__ uint32_t red_amax[kLinSplit][MT * 16];
     __shared__ float row_s[MT * 16];
+    lds_poison(red);
+    lds_poison(red_amax);
+    lds_poison(row_s);
+    lds_poison_done();
 
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int n0 = blockIdx.x * 16;

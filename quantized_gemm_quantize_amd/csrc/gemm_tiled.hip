@@ -226,6 +226,8 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_tiled_kernel(
     constexpr int STAGE = (BM + BN) * CPR;   // uint4 slots per stage
     static_assert(BM * BN * 2 <= STAGES * STAGE * 16, "bf16 tile fits in the stage buffers");
     __shared__ uint4 lds[STAGES * STAGE];
+    lds_poison(lds);
+    lds_poison_done();
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;

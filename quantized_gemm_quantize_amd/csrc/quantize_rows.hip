@@ -45,6 +45,8 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
     const T *__restrict__ x, int64_t M, int K, int8_t *__restrict__ xq, float *__restrict__ xs) {
     constexpr int kRowsPerBlock = kWavesPerBlock / WPR;
     __shared__ uint32_t red[kWavesPerBlock];
+    lds_poison(red);
+    lds_poison_done();
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int sub = wave % WPR;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + wave / WPR;
@@ -114,6 +116,8 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_persistent(
     float *__restrict__ xs) {
     constexpr int kRowsPerBlock = kWavesPerBlock / WPR;
     __shared__ uint32_t red[2][kWavesPerBlock];  // by iteration parity
+    lds_poison(red);
+    lds_poison_done();
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int sub = wave % WPR;
     const int nch = K >> 3;

@@ -100,6 +100,8 @@ __global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_kernel(
     const uint32_t *__restrict__ Meta, const float *__restrict__ sw, void *__restrict__ out,
     int M, int N, int K, int steps_per_wave) {
     __shared__ int red[kSplit][MT][4][kWave];
+    lds_poison(red);
+    lds_poison_done();
 
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int n0 = blockIdx.x * 16;
@@ -245,6 +247,8 @@ __global__ __launch_bounds__(kTThreads, 1) void sparse24_tiled_kernel(
     const uint32_t *__restrict__ Meta, const float *__restrict__ sw, void *__restrict__ out,
     int M, int N, int K, int tiles_m, int tiles_n) {
     __shared__ uint4 lds[kTStages * kTStage];
+    lds_poison(lds);
+    lds_poison_done();
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int wm = wave >> 1, wn = wave & 1;
 

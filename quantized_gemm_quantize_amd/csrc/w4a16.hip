@@ -148,6 +148,8 @@ __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_kernel(
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     uint16_t *__restrict__ out, int M, int N, int K, int G, int chunks_per_wave) {
     __shared__ float red[kSplit][MT][4][kWave];
+    w8a8::lds_poison(red);
+    w8a8::lds_poison_done();
 
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int n0 = blockIdx.x * 16;
@@ -252,6 +254,8 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
     static_assert(WM * WN * 2 * 4 <= (XBUF * XS + WBUF * WS) * 16, "bf16 tile fits in LDS");
     static_assert(TM >= 1 && TN >= 1 && 2 * NLD < 64, "wavefront tiles and the vmcnt range");
     __shared__ uint4 lds[XBUF * XS + WBUF * WS];
+    w8a8::lds_poison(lds);
+    w8a8::lds_poison_done();
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
