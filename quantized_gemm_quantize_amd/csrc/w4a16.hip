@@ -207,6 +207,118 @@ __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_kernel(
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+
+// Weight-streaming W4A16 GEMM for M <= 16 and K a multiple of 4096, with the
+// activations moved global -> LDS by 16-byte direct-to-LDS loads. At M = 16
+// every workgroup reads all 16 x K bf16 activations, four times the bytes of
+// its weight codes; loaded straight into the MFMA fragment layout (lane
+// quarter q takes 16-byte pieces 64 bytes apart) each load instruction
+// touched 32 cache lines a quarter used. Here one load instruction fills 64
+// LDS slots with 4 rows x 256 bytes of a 128-column chunk (8 whole lines).
+// Slot p of a row holds the row's 16-byte piece p ^ row, so the fragment
+// reads of the 16 lanes of a quarter (16 rows, one piece) hit 16 distinct
+// bank groups. Wavefront w takes chunks 4w .. 4w+3 of every 4096-column
+// block, issues all their loads at once (activations, codes, scale, zero per
+// chunk) and multiplies each chunk as soon as its loads have landed (vector
+// loads complete in order); each wavefront touches only its own LDS region.
+// Rows past M are read from row M - 1 and never stored.
+template <bool S4, bool F16>
+__global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_lds_kernel(
+    const uint16_t *__restrict__ X, const uint8_t *__restrict__ wq4,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    uint16_t *__restrict__ out, int M, int N, int K, int G) {
+    constexpr int kCpw = 4;                          // chunks per wavefront per block
+    constexpr int kBlockCols = kSplit * kCpw * 128;  // 4096 columns per block
+    constexpr int kChunkSlots = 16 * 16;             // 16 rows x 256 bytes
+    constexpr int kLoadsPerChunk = 7;                // 4 activation loads, codes, scale, zero
+    static_assert(kLoadsPerChunk * kCpw < 64, "vmcnt range");
+    // one LDS array per chunk position: the compiler then knows which loads in
+    // flight a fragment read may depend on, and waits for those only (with one
+    // array it waits for every direct-to-LDS load before the first read)
+    __shared__ uint4 lds0[kSplit * kChunkSlots], lds1[kSplit * kChunkSlots],
+        lds2[kSplit * kChunkSlots], lds3[kSplit * kChunkSlots];
+    __shared__ float red[kSplit][4][kWave];
+    w8a8::lds_poison(lds0);
+    w8a8::lds_poison(lds1);
+    w8a8::lds_poison(lds2);
+    w8a8::lds_poison(lds3);
+    w8a8::lds_poison(red);
+    w8a8::lds_poison_done();
+
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int n0 = blockIdx.x * 16;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int n = n0 + r16;
+    const uint8_t *wrow = wq4 + (int64_t)n * (K / 2) + 16 * q;
+    const uint16_t *srow = scales + (int64_t)n * (K / G), *zrow = zeros + (int64_t)n * (K / G);
+    // load i of a chunk: row 4 i + lane / 16, slot lane % 16 <- piece (lane % 16) ^ row
+    const uint16_t *xsrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * i + (lane >> 4);
+        xsrc[i] = X + (int64_t)min(row, M - 1) * K + 8 * ((lane & 15) ^ row);
+    }
+    uint4 *const region[kCpw] = {lds0 + wave * kChunkSlots, lds1 + wave * kChunkSlots,
+                                 lds2 + wave * kChunkSlots, lds3 + wave * kChunkSlots};
+
+    v4f acc = v4f{};
+    for (int kb = 0; kb < K; kb += kBlockCols) {
+        const int c0 = (kb >> 7) + wave * kCpw;
+        uint4 codes[kCpw];
+        uint16_t sv[kCpw], zv[kCpw];
+#pragma unroll
+        for (int j = 0; j < kCpw; ++j) {
+            const int c = c0 + j;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds((global_void *)(xsrc[i] + 128 * c),
+                                                 (lds_void *)(region[j] + 64 * i), 16, 0, 0);
+            codes[j] = load16_stream(wrow + 64 * c);
+            const int g = (128 * c + 32 * q) / G;
+            sv[j] = srow[g];
+            zv[j] = zrow[g];
+            __builtin_amdgcn_sched_barrier(0);  // chunk by chunk, in this order
+        }
+#pragma unroll
+        for (int j = 0; j < kCpw; ++j) {
+            if (j == 0) W4A16_WAIT_VM(kLoadsPerChunk * (kCpw - 1));
+            else if (j == 1) W4A16_WAIT_VM(kLoadsPerChunk * (kCpw - 2));
+            else if (j == 2) W4A16_WAIT_VM(kLoadsPerChunk * (kCpw - 3));
+            else W4A16_WAIT_VM(0);
+            asm volatile("" ::: "memory");
+            // nothing of this chunk (the dequantization of its codes included)
+            // moves above its wait, nor below the next chunk's
+            __builtin_amdgcn_sched_barrier(0);
+            const float s = h_to_float<F16>(sv[j]), z = h_to_float<F16>(zv[j]);
+            const uint32_t cw[4] = {codes[j].x, codes[j].y, codes[j].z, codes[j].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint4 b = region[j][16 * r16 + ((4 * q + t) ^ r16)];
+                acc = mfma16x16x32<F16>(dequant8<S4, F16>(cw[t], s, z), b, acc);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // every fragment of this block was read (the MFMAs consumed them)
+        // before the next block's loads refill the region
+    }
+
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    // one output per thread: channel ch of row j sits in lane j + 16 * (ch / 4),
+    // element ch % 4; the K-split partials add in fp32 in wavefront order
+    if (threadIdx.x >= 256) return;
+    const int j = threadIdx.x >> 4, ch = threadIdx.x & 15;
+    if (j >= M) return;
+    const int l = j + 16 * (ch >> 2), r = ch & 3;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSplit; ++w) sum += red[w][r][l];
+    out[(int64_t)j * N + n0 + ch] = (uint16_t)(pack_h2<F16>(sum, 0.0f) & 0xFFFFu);
+}
+
 template <int MT, bool S4, bool F16>
 hipError_t launch_decode_mt(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
                             const uint16_t *zeros, int N, int K, int G, uint16_t *out,
@@ -232,8 +344,6 @@ hipError_t launch_decode_mt(const uint16_t *x, int M, const uint8_t *wq4, const 
 // wait only for the stage that must be complete (counted vector-memory waits,
 // no fence): loads of later stages stay in flight across them.
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void global_void;
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
@@ -479,6 +589,11 @@ template <bool S4, bool F16>
 hipError_t launch_gemm_codes(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
                              const uint16_t *zeros, int N, int K, int G, uint16_t *out,
                              hipStream_t stream) {
+    if (M <= 16 && K % 4096 == 0) {
+        w4a16_decode_lds_kernel<S4, F16><<<dim3((unsigned)(N / 16)), dim3(kSplit * kWave), 0, stream>>>(
+            x, wq4, scales, zeros, out, M, N, K, G);
+        return hipGetLastError();
+    }
     switch ((M + 15) / 16) {
         case 1: return launch_decode_mt<1, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
         case 2: return launch_decode_mt<2, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);

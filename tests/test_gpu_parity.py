@@ -641,9 +641,10 @@ def _w4a16_case(b, oracle, inp, what, rows=None, signed=False):
 
 
 @pytest.mark.parametrize("M,N,K,G", [
-    # weight-streaming path (M <= 64)
+    # weight-streaming path (M <= 64); M <= 16 with K a multiple of 4096 takes the kernel
+    # that moves the activations through LDS (one and two 4096-column blocks, ragged M)
     (1, 16, 128, 128), (5, 48, 256, 32), (16, 128, 4096, 128), (17, 64, 640, 64),
-    (33, 32, 1024, 256), (64, 96, 512, 128),
+    (33, 32, 1024, 256), (64, 96, 512, 128), (1, 32, 4096, 128), (9, 64, 8192, 256),
     # tiled path: 64 x 64 tiles (ragged M and N), 128 x 64 and 256 x 64 tiles (256+ of them)
     (65, 64, 128, 128), (100, 80, 384, 32), (130, 272, 1024, 64), (257, 528, 256, 128),
     (400, 4160, 256, 64), (300, 8192, 128, 32),
@@ -656,7 +657,7 @@ def test_w4a16_gemm_shapes(b, oracle, M, N, K, G):
 
 @pytest.mark.parametrize("M,N,K,G", [(16, 128, 4096, 128), (33, 32, 1024, 256),
                                      (130, 272, 1024, 64), (400, 4160, 256, 64),
-                                     (1024, 4112, 256, 64)])
+                                     (1024, 4112, 256, 64), (7, 48, 8192, 128)])
 def test_w4a16_gemm_signed_codes(b, oracle, M, N, K, G):
     """s4 codes on each kernel path (weight streaming, 64x64, 128x64 and 256x64 tiles)."""
     log(f"w4a16 gemm s4 M={M} N={N} K={K} G={G}")
