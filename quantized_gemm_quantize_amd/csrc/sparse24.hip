@@ -30,6 +30,13 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
+// s_waitcnt on the vector-memory counter only
+template <int N>
+__device__ __forceinline__ void wait_vm_s24() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 __device__ __forceinline__ v4i smfmac_16x16x128(v4i a, v8i b, v4i c, int idx) {
     return __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, c, idx, 0, 0);
 }
@@ -172,6 +179,113 @@ __global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_kernel(
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+
+// The same for M <= 16 and K a multiple of 4096, with the activations moved
+// global -> LDS. Each workgroup reads all 16 x K activation bytes, twice the
+// bytes of its compressed weights; loaded straight into the operand layout
+// (32 bytes per lane, 16 rows x 4 pieces per instruction) each load touched
+// 16 half-used lines. Here one direct-to-LDS instruction fills 64 slots with 8
+// rows x 128 bytes of a block (8 whole lines); slot p of a row holds its
+// 16-byte piece p ^ (row / 2), so the two fragment reads of the 16 lanes of a
+// quarter (rows 0..15, one piece each) hit 16 distinct bank groups. Wavefront
+// w takes blocks 4w .. 4w+3 of every 4096-column K block and issues all their
+// loads at once (activations, values, index word per block), each block
+// multiplied after its own wait; one LDS array per block position, so the
+// compiler's waits match these (see the dense M-small kernel). Rows past M
+// are read from row M - 1 and never stored.
+template <bool OUT_I32>
+__global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_lds_kernel(
+    const int8_t *__restrict__ X, const float *__restrict__ sx, const int8_t *__restrict__ V,
+    const uint32_t *__restrict__ Meta, const float *__restrict__ sw, void *__restrict__ out,
+    int M, int N, int K) {
+    constexpr int kBpw = 4;                        // blocks per wavefront per K block
+    constexpr int kKBlock = kSplit * kBpw * 128;   // 4096 columns
+    constexpr int kBlockSlots = 16 * 8;            // 16 rows x 128 bytes
+    constexpr int kLoadsPerBlock = 4;              // 2 activation loads, values, index word
+    __shared__ uint4 b0[kSplit * kBlockSlots], b1[kSplit * kBlockSlots], b2[kSplit * kBlockSlots],
+        b3[kSplit * kBlockSlots];
+    __shared__ int red[kSplit][4][kWave];
+    lds_poison(b0);
+    lds_poison(b1);
+    lds_poison(b2);
+    lds_poison(b3);
+    lds_poison(red);
+    lds_poison_done();
+
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int n0 = blockIdx.x * 16;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int half = q >> 1, sub = q & 1;
+    const int8_t *vrow = V + (int64_t)(n0 + r16) * 64 + 32 * sub + 16 * half;
+    const uint32_t *mrow = Meta + (int64_t)(n0 + r16) * 4 + 2 * sub + half;
+    const int64_t vstride = (int64_t)N * 64, mstride = (int64_t)N * 4;   // per block
+    // activation load h of a block: row 8 h + lane / 8, slot lane % 8 <- piece (lane % 8) ^ (row / 2)
+    const int8_t *xsrc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = 8 * h + (lane >> 3);
+        xsrc[h] = X + (int64_t)min(row, M - 1) * K + 16 * ((lane & 7) ^ (row >> 1));
+    }
+    uint4 *const region[kBpw] = {b0 + wave * kBlockSlots, b1 + wave * kBlockSlots,
+                                 b2 + wave * kBlockSlots, b3 + wave * kBlockSlots};
+    // fragment: lane (r16, q) takes pieces 2q and 2q + 1 of row r16
+    const int f0 = 8 * r16 + ((2 * q) ^ (r16 >> 1)), f1 = 8 * r16 + ((2 * q + 1) ^ (r16 >> 1));
+
+    v4i acc = v4i{};
+    for (int kb = 0; kb < K; kb += kKBlock) {
+        const int blk0 = (kb >> 7) + wave * kBpw;
+        v4i a[kBpw];
+        int idx[kBpw];
+#pragma unroll
+        for (int j = 0; j < kBpw; ++j) {
+            const int blk = blk0 + j;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                __builtin_amdgcn_global_load_lds((global_void *)(xsrc[h] + 128 * blk),
+                                                 (lds_void *)(region[j] + 64 * h), 16, 0, 0);
+            a[j] = __builtin_bit_cast(v4i, load16_stream(vrow + blk * vstride));
+            idx[j] = (int)mrow[blk * mstride];
+            __builtin_amdgcn_sched_barrier(0);  // block by block, in this order
+        }
+#pragma unroll
+        for (int j = 0; j < kBpw; ++j) {
+            if (j == 0) wait_vm_s24<kLoadsPerBlock * (kBpw - 1)>();
+            else if (j == 1) wait_vm_s24<kLoadsPerBlock * (kBpw - 2)>();
+            else if (j == 2) wait_vm_s24<kLoadsPerBlock * (kBpw - 3)>();
+            else wait_vm_s24<0>();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            const uint4 lo = region[j][f0], hi = region[j][f1];
+            const v8i b = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                           (int)hi.w};
+            acc = smfmac_16x16x128(a[j], b, acc, idx[j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // every fragment of this block was read before the next block's
+        // loads refill the regions (the MFMAs consumed them)
+    }
+
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    // one output per thread: channel c of row j sits in lane j + 16 * (c / 4), element c % 4
+    if (threadIdx.x >= 256) return;
+    const int j = threadIdx.x >> 4, c = threadIdx.x & 15;
+    if (j >= M) return;
+    const int l = j + 16 * (c >> 2), r = c & 3;
+    int sum = 0;
+#pragma unroll
+    for (int w = 0; w < kSplit; ++w) sum += red[w][r][l];
+    const int n = n0 + c;
+    if constexpr (OUT_I32)
+        static_cast<int32_t *>(out)[(int64_t)j * N + n] = sum;
+    else
+        static_cast<__bf16 *>(out)[(int64_t)j * N + n] =
+            (__bf16)dequant(sum, split_scale(sx[j]), split_scale(sw[n]));
+}
+
 template <int MT>
 hipError_t launch_decode_mt(const int8_t *xq, const float *xs, int M, const int8_t *values,
                             const uint32_t *meta, const float *ws, int N, int K, void *out,
@@ -225,8 +339,6 @@ static_assert(kTXLd * 256 == kTXSlots && kTVLd * 256 == kTVSlots && kTMLd * 256 
               "whole runs per wavefront");
 static_assert(kTBM * kTBN * 2 <= kTStages * kTStage * 16, "bf16 tile fits in the stage buffers");
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void global_void;
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int vswz(int row) { return (row >> 1) & 3; }
@@ -463,6 +575,14 @@ hipError_t launch_compress24(const int8_t *wq, int N, int K, int8_t *values, uin
 hipError_t launch_sparse24_gemm(const int8_t *xq, const float *xs, int M, const int8_t *values,
                                 const uint32_t *meta, const float *ws, int N, int K, void *out,
                                 bool out_i32, hipStream_t stream) {
+    if (M <= 16 && K % 4096 == 0) {
+        const dim3 grid((unsigned)(N / 16)), block(kSplit * kWave);
+        if (out_i32)
+            sparse24_decode_lds_kernel<true><<<grid, block, 0, stream>>>(xq, xs, values, meta, ws, out, M, N, K);
+        else
+            sparse24_decode_lds_kernel<false><<<grid, block, 0, stream>>>(xq, xs, values, meta, ws, out, M, N, K);
+        return hipGetLastError();
+    }
     switch ((M + 15) / 16) {
         case 1: return launch_decode_mt<1>(xq, xs, M, values, meta, ws, N, K, out, out_i32, stream);
         case 2: return launch_decode_mt<2>(xq, xs, M, values, meta, ws, N, K, out, out_i32, stream);

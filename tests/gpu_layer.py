@@ -44,6 +44,15 @@ def make_layer(b):
     t["wq4"] = _dev(w4.wq4)
     t["s4"] = _bf16(w4.scales)
     t["z4"] = _bf16(w4.zeros)
+    # the M-small 2:4 and W4A16 kernels that move activations through LDS (K = KL)
+    spl = make_linear(MD, N, KL, seed=27, sparse24=True)
+    wq24l, t["sw24l"] = b.w8a8_quantize_rows_f32(_dev(spl.w))
+    t["v24l"], t["m24l"] = b.w8a8_compress24(wq24l)
+    w4l = make_w4a16(MD, N, KL, 128, seed=28)
+    t["x4l"] = _bf16(w4l.x_bits)
+    t["wq4l"] = _dev(w4l.wq4)
+    t["s4l"] = _bf16(w4l.scales)
+    t["z4l"] = _bf16(w4l.zeros)
     # outputs (written by every run)
     t["xq"] = torch.empty((M, K), dtype=torch.int8, device=DEV)
     t["sx"] = torch.empty((M,), dtype=torch.float32, device=DEV)
@@ -53,8 +62,8 @@ def make_layer(b):
     t["sxl"] = torch.empty((MD,), dtype=torch.float32, device=DEV)
     for name, rows in (("gemm", M), ("addmm", M), ("dec", MD), ("dec_addmm", MD), ("fused", MD),
                        ("decl", MD), ("decl_addmm", MD),
-                       ("bsr", M), ("bsr_addmm", M), ("s24", M), ("s24d", MD), ("w4", M),
-                       ("w4d", MD)):
+                       ("bsr", M), ("bsr_addmm", M), ("s24", M), ("s24d", MD), ("s24dl", MD),
+                       ("w4", M), ("w4d", MD), ("w4dl", MD)):
         t["out_" + name] = torch.empty((rows, N), dtype=torch.bfloat16, device=DEV)
     torch.cuda.synchronize()
     return t
@@ -62,7 +71,7 @@ def make_layer(b):
 
 OUTPUTS = ["xq", "sx", "xqd", "sxd", "xql", "sxl", "out_gemm", "out_addmm", "out_dec",
            "out_dec_addmm", "out_decl", "out_decl_addmm", "out_fused", "out_bsr", "out_bsr_addmm",
-           "out_s24", "out_s24d", "out_w4", "out_w4d"]
+           "out_s24", "out_s24d", "out_s24dl", "out_w4", "out_w4d", "out_w4dl"]
 
 
 def run_layer(b, t, stream=None):
@@ -92,6 +101,9 @@ def run_layer(b, t, stream=None):
                          stream=stream)
     b.w4a16_gemm(t["x4"], t["wq4"], t["s4"], t["z4"], out=t["out_w4"], stream=stream)
     b.w4a16_gemm(t["x4"][:MD], t["wq4"], t["s4"], t["z4"], out=t["out_w4d"], stream=stream)
+    b.w8a8_sparse24_gemm(t["xql"], t["sxl"], t["v24l"], t["m24l"], t["sw24l"], out=t["out_s24dl"],
+                         stream=stream)
+    b.w4a16_gemm(t["x4l"], t["wq4l"], t["s4l"], t["z4l"], out=t["out_w4dl"], stream=stream)
 
 
 def clear_outputs(t):

@@ -506,9 +506,10 @@ def _sparse24_case(b, oracle, M, N, K, seed, rows=None):
 
 
 SPARSE24_SHAPES = [
-    # weight-streaming path (M <= 64)
+    # weight-streaming path (M <= 64); M <= 16 with K a multiple of 4096 moves the
+    # activations through LDS (one and two 4096-column blocks, ragged M)
     (1, 16, 128), (5, 48, 384), (3, 1040, 128), (16, 128, 4096), (17, 64, 640), (33, 32, 128),
-    (48, 160, 1152), (64, 96, 512), (64, 256, 8192),
+    (48, 160, 1152), (64, 96, 512), (64, 256, 8192), (1, 32, 4096), (9, 64, 8192),
     # tiled path (128 x 256 tiles): ragged M and N, one and many tiles and stages
     (65, 256, 128), (129, 16, 128), (130, 272, 384), (300, 528, 256), (520, 1040, 1152),
     (256, 512, 4096), (1100, 2064, 640),
