@@ -507,15 +507,15 @@ hipError_t launch_lds(const int8_t *xq, const float *xs, int M, const int8_t *wq
 }
 
 // M <= 16 with K a multiple of the 4096-byte LDS block: both operands through
-// LDS (K = N = 4096, M = 16: 5.85 us against 6.7 us for the register-path
-// kernel; K = 8192 with 16 wavefronts 9.2 against 11.4 us). At M = 1 the
-// register path's activation reads cost nothing and it stays ahead (5.1
-// against 5.4 us), as it does for short or ragged K, whose masked steps would
-// fill a whole LDS block.
+// LDS (K = N = 4096, M = 16: 5.15 us against 6.7 us for the register-path
+// kernel; M = 1: 4.6 against 5.3 us, although every activation row slot then
+// repeats row 0; K = 8192 with 16 wavefronts 8.7 against 11.4 us). Short or
+// ragged K keeps the register path: its masked steps would fill a whole LDS
+// block.
 hipError_t launch_gemm_decode(const int8_t *xq, const float *xs, int M, const int8_t *wq,
                               const float *ws, int N, int K, void *out, bool out_i32,
                               hipStream_t stream, const Addmm *am) {
-    if (M > 1 && M <= 16 && K % 4096 == 0) {
+    if (M <= 16 && K % 4096 == 0) {
         if (K == 4096) return launch_lds<4>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
         return launch_lds<16>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
     }
