@@ -506,17 +506,19 @@ hipError_t launch_lds(const int8_t *xq, const float *xs, int M, const int8_t *wq
     return hipGetLastError();
 }
 
-// M <= 16 with K a multiple of the 4096-byte LDS block: both operands through
-// LDS (K = N = 4096, M = 16: 5.15 us against 6.7 us for the register-path
-// kernel; M = 1: 4.6 against 5.3 us, although every activation row slot then
-// repeats row 0; K = 8192 with 16 wavefronts 8.7 against 11.4 us). Short or
-// ragged K keeps the register path: its masked steps would fill a whole LDS
-// block.
+// M <= 16 with K >= 3072: both operands through LDS, 4 wavefronts up to one
+// 4096-byte block and 16 beyond (K = N = 4096, M = 16: 5.15 us against 6.7 us
+// for the register-path kernel; M = 1: 4.6 against 5.3 us, although every
+// activation row slot then repeats row 0; K = 8192: 8.7 against 11.4 us). A
+// ragged last block is masked and still wins (K = 11008: 11.8 against 16.1 us,
+// K = 5120: 7.35 against 9.9 us, K = 3072: 5.0 against 6.2 us); below 3072 the
+// masked part of the block costs more than the LDS path saves (K = 1024: 3.9
+// against 3.5 us), so short K keeps the register path.
 hipError_t launch_gemm_decode(const int8_t *xq, const float *xs, int M, const int8_t *wq,
                               const float *ws, int N, int K, void *out, bool out_i32,
                               hipStream_t stream, const Addmm *am) {
-    if (M <= 16 && K % 4096 == 0) {
-        if (K == 4096) return launch_lds<4>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
+    if (M <= 16 && K >= 3072) {
+        if (K <= 4096) return launch_lds<4>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
         return launch_lds<16>(xq, xs, M, wq, ws, N, K, out, out_i32, stream, am);
     }
     switch ((M + 15) / 16) {

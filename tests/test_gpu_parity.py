@@ -140,10 +140,10 @@ GEMM_SHAPES = [
     (1100, 2064, 272), (129, 16, 16),
     # M-small shapes with K long enough for the 2- and 4-wavefront splits, ragged K tails
     (16, 64, 4112), (1, 32, 8208), (32, 48, 4096), (20, 16, 6160),
-    # both operands through LDS (M <= 16, K a multiple of 4096): one block with 4
-    # wavefronts, several blocks with 16
+    # both operands through LDS (M <= 16, K >= 3072): one block with 4 wavefronts,
+    # several blocks with 16, ragged last blocks (3072, 5120, 11008; 4112 and 8208 above)
     (16, 80, 4096), (2, 32, 4096), (9, 48, 4096), (16, 64, 8192), (5, 16, 12288),
-    (1, 48, 4096), (1, 32, 8192),
+    (1, 48, 4096), (1, 32, 8192), (16, 64, 3072), (9, 48, 5120), (3, 32, 11008),
 ]
 
 
