@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_kernel(
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 
-// The same for M <= 16 and K a multiple of 4096, with the activations moved
+// The same for M <= 16 and K >= 4096, with the activations moved
 // global -> LDS. Each workgroup reads all 16 x K activation bytes, twice the
 // bytes of its compressed weights; loaded straight into the operand layout
 // (32 bytes per lane, 16 rows x 4 pieces per instruction) each load touched
@@ -194,7 +194,8 @@ typedef __attribute__((address_space(1))) void global_void;
 // loads at once (activations, values, index word per block), each block
 // multiplied after its own wait; one LDS array per block position, so the
 // compiler's waits match these (see the dense M-small kernel). Rows past M
-// are read from row M - 1 and never stored.
+// are read from row M - 1 and never stored; blocks past K (a ragged last K
+// block) load the last block again and are not multiplied.
 template <bool OUT_I32>
 __global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_lds_kernel(
     const int8_t *__restrict__ X, const float *__restrict__ sx, const int8_t *__restrict__ V,
@@ -233,6 +234,7 @@ __global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_lds_kernel(
     // fragment: lane (r16, q) takes pieces 2q and 2q + 1 of row r16
     const int f0 = 8 * r16 + ((2 * q) ^ (r16 >> 1)), f1 = 8 * r16 + ((2 * q + 1) ^ (r16 >> 1));
 
+    const int nblk = K / 128;
     v4i acc = v4i{};
     for (int kb = 0; kb < K; kb += kKBlock) {
         const int blk0 = (kb >> 7) + wave * kBpw;
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_lds_kernel(
         int idx[kBpw];
 #pragma unroll
         for (int j = 0; j < kBpw; ++j) {
-            const int blk = blk0 + j;
+            const int blk = min(blk0 + j, nblk - 1);
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 __builtin_amdgcn_global_load_lds((global_void *)(xsrc[h] + 128 * blk),
@@ -257,6 +259,7 @@ __global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_lds_kernel(
             else wait_vm_s24<0>();
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
+            if (blk0 + j >= nblk) continue;  // past K (uniform per wavefront)
             const uint4 lo = region[j][f0], hi = region[j][f1];
             const v8i b = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
                            (int)hi.w};
@@ -575,7 +578,7 @@ hipError_t launch_compress24(const int8_t *wq, int N, int K, int8_t *values, uin
 hipError_t launch_sparse24_gemm(const int8_t *xq, const float *xs, int M, const int8_t *values,
                                 const uint32_t *meta, const float *ws, int N, int K, void *out,
                                 bool out_i32, hipStream_t stream) {
-    if (M <= 16 && K % 4096 == 0) {
+    if (M <= 16 && K >= 4096) {
         const dim3 grid((unsigned)(N / 16)), block(kSplit * kWave);
         if (out_i32)
             sparse24_decode_lds_kernel<true><<<grid, block, 0, stream>>>(xq, xs, values, meta, ws, out, M, N, K);

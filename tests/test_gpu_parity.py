@@ -511,6 +511,7 @@ SPARSE24_SHAPES = [
     # activations through LDS (one and two 4096-column blocks, ragged M)
     (1, 16, 128), (5, 48, 384), (3, 1040, 128), (16, 128, 4096), (17, 64, 640), (33, 32, 128),
     (48, 160, 1152), (64, 96, 512), (64, 256, 8192), (1, 32, 4096), (9, 64, 8192),
+    (7, 32, 5120), (16, 48, 4224),
     # tiled path (128 x 256 tiles): ragged M and N, one and many tiles and stages
     (65, 256, 128), (129, 16, 128), (130, 272, 384), (300, 528, 256), (520, 1040, 1152),
     (256, 512, 4096), (1100, 2064, 640),
@@ -647,6 +648,7 @@ def _w4a16_case(b, oracle, inp, what, rows=None, signed=False):
     # that moves the activations through LDS (one and two 4096-column blocks, ragged M)
     (1, 16, 128, 128), (5, 48, 256, 32), (16, 128, 4096, 128), (17, 64, 640, 64),
     (33, 32, 1024, 256), (64, 96, 512, 128), (1, 32, 4096, 128), (9, 64, 8192, 256),
+    (5, 48, 4224, 128), (16, 32, 6144, 64),
     # tiled path: 64 x 64 tiles (ragged M and N), 128 x 64 and 256 x 64 tiles (256+ of them)
     (65, 64, 128, 128), (100, 80, 384, 32), (130, 272, 1024, 64), (257, 528, 256, 128),
     (400, 4160, 256, 64), (300, 8192, 128, 32),
