@@ -195,7 +195,7 @@ typedef __attribute__((address_space(1))) void global_void;
 // multiplied after its own wait; one LDS array per block position, so the
 // compiler's waits match these (see the dense M-small kernel). Rows past M
 // are read from row M - 1 and never stored; blocks past K (a ragged last K
-// block) load the last block again and are not multiplied.
+// block) load the last block again and multiply zero values.
 template <bool OUT_I32>
 __global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_lds_kernel(
     const int8_t *__restrict__ X, const float *__restrict__ sx, const int8_t *__restrict__ V,
@@ -259,11 +259,13 @@ __global__ __launch_bounds__(kSplit *kWave) void sparse24_decode_lds_kernel(
             else wait_vm_s24<0>();
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            if (blk0 + j >= nblk) continue;  // past K (uniform per wavefront)
+            // a block past K multiplies zero values (a select, not a branch:
+            // see the W4A16 kernel)
+            const v4i av = blk0 + j < nblk ? a[j] : v4i{};
             const uint4 lo = region[j][f0], hi = region[j][f1];
             const v8i b = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
                            (int)hi.w};
-            acc = smfmac_16x16x128(a[j], b, acc, idx[j]);
+            acc = smfmac_16x16x128(av, b, acc, idx[j]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // every fragment of this block was read before the next block's

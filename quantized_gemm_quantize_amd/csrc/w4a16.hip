@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_kernel(
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 
-// Weight-streaming W4A16 GEMM for M <= 16 and K >= 4096, with the
+// Weight-streaming W4A16 GEMM for M <= 16 and K a multiple of 4096, with the
 // activations moved global -> LDS by 16-byte direct-to-LDS loads. At M = 16
 // every workgroup reads all 16 x K bf16 activations, four times the bytes of
 // its weight codes; loaded straight into the MFMA fragment layout (lane
@@ -223,8 +223,7 @@ typedef __attribute__((address_space(1))) void global_void;
 // block, issues all their loads at once (activations, codes, scale, zero per
 // chunk) and multiplies each chunk as soon as its loads have landed (vector
 // loads complete in order); each wavefront touches only its own LDS region.
-// Rows past M are read from row M - 1 and never stored; chunks past K (a
-// ragged last block) load the last chunk again and are not multiplied.
+// Rows past M are read from row M - 1 and never stored.
 template <bool S4, bool F16>
 __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_lds_kernel(
     const uint16_t *__restrict__ X, const uint8_t *__restrict__ wq4,
@@ -264,7 +263,6 @@ __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_lds_kernel(
     uint4 *const region[kCpw] = {lds0 + wave * kChunkSlots, lds1 + wave * kChunkSlots,
                                  lds2 + wave * kChunkSlots, lds3 + wave * kChunkSlots};
 
-    const int nchunks = K / 128;
     v4f acc = v4f{};
     for (int kb = 0; kb < K; kb += kBlockCols) {
         const int c0 = (kb >> 7) + wave * kCpw;
@@ -272,7 +270,7 @@ __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_lds_kernel(
         uint16_t sv[kCpw], zv[kCpw];
 #pragma unroll
         for (int j = 0; j < kCpw; ++j) {
-            const int c = min(c0 + j, nchunks - 1);
+            const int c = c0 + j;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 __builtin_amdgcn_global_load_lds((global_void *)(xsrc[i] + 128 * c),
@@ -293,7 +291,6 @@ __global__ __launch_bounds__(kSplit *kWave) void w4a16_decode_lds_kernel(
             // nothing of this chunk (the dequantization of its codes included)
             // moves above its wait, nor below the next chunk's
             __builtin_amdgcn_sched_barrier(0);
-            if (c0 + j >= nchunks) continue;  // past K (uniform per wavefront)
             const float s = h_to_float<F16>(sv[j]), z = h_to_float<F16>(zv[j]);
             const uint32_t cw[4] = {codes[j].x, codes[j].y, codes[j].z, codes[j].w};
 #pragma unroll
@@ -592,7 +589,7 @@ template <bool S4, bool F16>
 hipError_t launch_gemm_codes(const uint16_t *x, int M, const uint8_t *wq4, const uint16_t *scales,
                              const uint16_t *zeros, int N, int K, int G, uint16_t *out,
                              hipStream_t stream) {
-    if (M <= 16 && K >= 4096) {
+    if (M <= 16 && K % 4096 == 0) {
         w4a16_decode_lds_kernel<S4, F16><<<dim3((unsigned)(N / 16)), dim3(kSplit * kWave), 0, stream>>>(
             x, wq4, scales, zeros, out, M, N, K, G);
         return hipGetLastError();
