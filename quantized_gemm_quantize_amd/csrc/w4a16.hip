@@ -330,25 +330,28 @@ hipError_t launch_decode_mt(const uint16_t *x, int M, const uint8_t *wq4, const 
 }
 
 // ---------------------------------------------------------------------------
-// LDS-tiled W4A16 GEMM for M > 64: BM x BN tile per workgroup of 4 wavefronts
-// (2 x 2, v_mfma_f32_32x32x16_bf16, weights first), K advancing 64 columns
-// per stage. Activations move global -> LDS with direct-to-LDS 16-byte loads
-// through a ring of 4 stages (issued 3 stages ahead); the weight codes of a
-// stage are loaded into registers 2 stages ahead, dequantized once per
-// workgroup into one of two bf16 weight buffers in LDS a stage before they
-// are used, and read there by every wavefront of the tile (the dequant
-// arithmetic per weight is shared by the tile's BM rows). The dequantization
-// of stage s + 1 is interleaved with the MFMAs of stage s, so the vector ALU
-// and the matrix cores work at once. Rows of 64 bf16 are 128 bytes, chunk c of
-// row r at slot c ^ (r % 8) ^ ((r / 8) % 2), as in the int8 kernel. Barriers
-// wait only for the stage that must be complete (counted vector-memory waits,
-// no fence): loads of later stages stay in flight across them.
+// LDS-tiled W4A16 GEMM for M > 64: BM x BN tile per workgroup of 8 wavefronts
+// in two roles, K advancing 64 columns per stage. Wavefronts 0-3 (2 x 2 or
+// 4 x 1 over the tile, v_mfma_f32_32x32x16_bf16, weights first) move the
+// activations global -> LDS with direct-to-LDS 16-byte loads through a ring of
+// 4 stages (issued 3 stages ahead) and run the MFMAs. Wavefronts 4-7 load the
+// weight codes of a stage into registers 2 stages ahead and dequantize them
+// once per workgroup into one of two bf16 weight buffers in LDS a stage before
+// they are used (the dequant arithmetic per weight is shared by the tile's BM
+// rows). Each SIMD holds one wavefront of each role, so one's MFMAs and the
+// other's dequantization overlap; a single role doing both took about the sum
+// of the two per stage. Rows of 64 bf16 are 128 bytes, chunk c of row r at
+// slot c ^ (r % 8) ^ ((r / 8) % 2), as in the int8 kernel. Each role waits
+// only for its own loads of the stage that must be complete (counted
+// vector-memory waits, no fence), then both meet at the stage barrier: loads
+// of later stages stay in flight across it. Both roles pass the same barriers
+// (one after the prologue, one per stage, two at the end).
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 template <int BM, int BN, int WAVES_M, bool S4, bool F16>
-__global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
+__global__ __launch_bounds__(512, 1) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ X, const uint8_t *__restrict__ wq4,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     uint16_t *__restrict__ out, int M, int N, int K, int G, int tiles_m, int tiles_n) {
@@ -358,17 +361,22 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
     constexpr int XBUF = 4, WBUF = 2;
     constexpr int XLD = XS / 256;                              // activation loads per wavefront
     constexpr int CODES = BN * 64 / 256;                       // weight codes per thread per stage
-    constexpr int CLD = CODES == 64 ? 2 : 1;                   // 16-byte code loads (or one 8-byte)
-    constexpr int NLD = XLD + CLD + 2;                         // + codes, scale, zero
-    static_assert(CODES == 64 || CODES == 32 || CODES == 16, "32, 16 or 8 bytes of codes per thread");
+    constexpr int NC = 3;                                      // code loads per stage: codes, scale, zero
+    // a thread's codes lie in one group: CODES consecutive columns starting at a
+    // multiple of CODES, and G is a multiple of 32
+    static_assert(CODES == 32 || CODES == 16, "16 or 8 bytes of codes per thread");
     static_assert(WM * WN * 2 * 4 <= (XBUF * XS + WBUF * WS) * 16, "bf16 tile fits in LDS");
-    static_assert(TM >= 1 && TN >= 1 && 2 * NLD < 64, "wavefront tiles and the vmcnt range");
+    static_assert(TM >= 1 && TN >= 1 && 2 * XLD < 64, "wavefront tiles and the vmcnt range");
     __shared__ uint4 lds[XBUF * XS + WBUF * WS];
     w8a8::lds_poison(lds);
     w8a8::lds_poison_done();
 
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    // mwave: the wavefront's place among the four that multiply; ct: the
+    // thread's place among the 256 that dequantize
+    const int wave = tid / kWave, mwave = wave & 3, ct = tid & 255;
+    const bool math = wave < 4;  // uniform per wavefront
+    const int wm = mwave / WAVES_N, wn = mwave % WAVES_N;
     const int tiles = tiles_m * tiles_n;
     const int t = w8a8::xcd_contiguous(blockIdx.x, tiles);
     constexpr int kGroup = 4;
@@ -378,182 +386,197 @@ __global__ __launch_bounds__(256, 1) void w4a16_tiled_kernel(
     const int m0 = (first_m + (t % per_group) % gsize) * BM;
     const int n0 = ((t % per_group) / gsize) * BN;
     const int nk = K / 64;
-
-    // activation loads: load l of this wavefront fills slots 64 (wave + 4 l) ..
-    const uint16_t *xsrc[XLD];
-    {
-        const int row = 8 * wave + (lane >> 3);
-        const int kc = (lane & 7) ^ swz(row);
-#pragma unroll
-        for (int l = 0; l < XLD; ++l) xsrc[l] = X + (int64_t)min(m0 + row + 32 * l, M - 1) * K + 8 * kc;
-    }
-    // weight codes: thread tid dequantizes columns [CODES * part, +CODES) of tile row wr
-    constexpr int PARTS = 64 / CODES;
-    const int wr = tid / PARTS, part = tid % PARTS;
-    const int64_t wn_row = min(n0 + wr, N - 1);
-    const uint8_t *wsrc = wq4 + wn_row * (K / 2) + part * (CODES / 2);
-    const uint16_t *ssrc = scales + wn_row * (K / G), *zsrc = zeros + wn_row * (K / G);
-
-    struct Codes {
-        uint32_t c[CODES / 8];
-        uint16_t s, z;
-    };
-    auto load_codes = [&](int j, Codes &c) {
-        const uint8_t *src = wsrc + 32 * j;
-        if constexpr (CODES == 64) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(src);
-            const uint4 u = *reinterpret_cast<const uint4 *>(src + 16);
-            c.c[0] = v.x; c.c[1] = v.y; c.c[2] = v.z; c.c[3] = v.w;
-            c.c[4] = u.x; c.c[5] = u.y; c.c[6] = u.z; c.c[7] = u.w;
-        } else if constexpr (CODES == 32) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(src);
-            c.c[0] = v.x; c.c[1] = v.y; c.c[2] = v.z; c.c[3] = v.w;
-        } else {
-            const uint2 v = *reinterpret_cast<const uint2 *>(src);
-            c.c[0] = v.x; c.c[1] = v.y;
-        }
-        const int g = (64 * j + part * CODES) / G;
-        c.s = ssrc[g];
-        c.z = zsrc[g];
-    };
+    const int last = nk - 1;
     auto xbuf = [&](int j) { return lds + (j % XBUF) * XS; };
     auto wbuf = [&](int j) { return lds + XBUF * XS + (j % WBUF) * WS; };
-    // word i of a thread's codes, dequantized into its weight buffer slot
-    auto store_word = [&](const Codes &c, int i, uint4 *__restrict__ wb) {
-        wb[wr * 8 + ((part * (CODES / 8) + i) ^ swz(wr))] =
-            dequant8<S4, F16>(c.c[i], h_to_float<F16>(c.s), h_to_float<F16>(c.z));
-    };
-    auto load_x = [&](int j, uint4 *__restrict__ buf) {
-#pragma unroll
-        for (int l = 0; l < XLD; ++l)
-            __builtin_amdgcn_global_load_lds((global_void *)(xsrc[l] + 64 * j),
-                                             (lds_void *)(buf + 64 * (wave + 4 * l)), 16, 0, 0);
-    };
 
-    const int frag_row = lane & 31, kh = lane >> 5;
-    const int fswz = swz(frag_row);
+    // The loops are straight-line: stages past the last are loaded from the
+    // last stage (in bounds) into buffers that are never read again, and the
+    // last dequantization writes a weight buffer last read two stages earlier.
+    // So every wait is for a fixed count (the loads of the 2 stages issued
+    // after the one that must be complete).
     v16f acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
-    // the MFMAs on buffers xb, wb, with the dequantization of `next` into weight
-    // buffer `nb` interleaved between the 4 K steps
-    auto compute = [&](const uint4 *__restrict__ xb, const uint4 *__restrict__ wb,
-                       const Codes &next, uint4 *__restrict__ nb) {
+    if (math) {
+        // activation loads: load l of this wavefront fills slots 64 (mwave + 4 l) ..
+        const uint16_t *xsrc[XLD];
+        {
+            const int row = 8 * mwave + (lane >> 3);
+            const int kc = (lane & 7) ^ swz(row);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = (2 * u + kh) ^ fswz;
-            uint4 xa[TM], wf[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                xa[i] = xb[(wm * WM + 32 * i + frag_row) * 8 + c];
-#pragma unroll
-            for (int q = 0; q < TN; ++q)
-                wf[q] = wb[(wn * WN + 32 * q + frag_row) * 8 + c];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int q = 0; q < TN; ++q)
-                    acc[i][q] = F16 ? __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                          __builtin_bit_cast(v8h, wf[q]), __builtin_bit_cast(v8h, xa[i]),
-                                          acc[i][q], 0, 0, 0)
-                                    : __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                          __builtin_bit_cast(v8bf, wf[q]), __builtin_bit_cast(v8bf, xa[i]),
-                                          acc[i][q], 0, 0, 0);
-            // this step's share of the code words (one or two; none in the
-            // last steps when there are only two)
-            constexpr int WPS = CODES / 8 > 4 ? CODES / 32 : 1;
-#pragma unroll
-            for (int i = 0; i < WPS; ++i)
-                if (u * WPS + i < CODES / 8) store_word(next, u * WPS + i, nb);
+            for (int l = 0; l < XLD; ++l)
+                xsrc[l] = X + (int64_t)min(m0 + row + 32 * l, M - 1) * K + 8 * kc;
         }
-    };
-
-    // The loop body is straight-line: stages past the last are loaded from the
-    // last stage (in bounds) into buffers that are never read again, and the
-    // last dequantization writes a weight buffer last read two stages earlier.
-    // So every barrier waits for a fixed count (the loads of the 2 stages issued
-    // after the one that must be complete) and the compiler's own waits before
-    // the dequantization are exact.
-    const int last = nk - 1;
-    // prologue: activations and codes of stages 0..2 in flight, stage 0
-    // dequantized; then stage 0 landed everywhere
-    Codes c0, c1, c2;
-    load_x(0, xbuf(0));
-    __builtin_amdgcn_sched_barrier(0);
-    load_codes(0, c0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_x(min(1, last), xbuf(1));
-    __builtin_amdgcn_sched_barrier(0);
-    load_codes(min(1, last), c1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_x(min(2, last), xbuf(2));
-    __builtin_amdgcn_sched_barrier(0);
-    load_codes(min(2, last), c2);
-    __builtin_amdgcn_sched_barrier(0);
+        auto load_x = [&](int j, uint4 *__restrict__ buf) {
 #pragma unroll
-    for (int i = 0; i < CODES / 8; ++i) store_word(c0, i, wbuf(0));
-    w8a8::vm_barrier<2 * NLD>();
-    // iteration s: issue stage s+3 (activations, codes into the registers that
-    // held stage s's codes, dequantized an iteration earlier), compute stage s
-    // while dequantizing stage s+1 (loaded two iterations earlier), then wait
-    // for stage s+1. Stage j's codes live in set j % 3; unrolling by 3 keeps
-    // that rotation free of register copies (a copy would wait for the load).
-    // The four buffers an iteration touches are distinct, and the restrict
-    // qualifiers say so: after inlining the accesses carry alias scopes, so the
-    // weight-buffer stores need not wait for the activation loads still landing
-    // in another buffer.
-    auto iteration = [&](int s, Codes &into, const Codes &deq, uint4 *__restrict__ xnew,
-                         const uint4 *__restrict__ xcur, const uint4 *__restrict__ wcur,
-                         uint4 *__restrict__ wnext) {
-        load_x(min(s + 3, last), xnew);
+            for (int l = 0; l < XLD; ++l)
+                __builtin_amdgcn_global_load_lds((global_void *)(xsrc[l] + 64 * j),
+                                                 (lds_void *)(buf + 64 * (mwave + 4 * l)), 16, 0, 0);
+        };
+        const int frag_row = lane & 31, kh = lane >> 5;
+        const int fswz = swz(frag_row);
+        // the MFMAs of a stage; the fragment reads of step u + 1 go out right
+        // after the first MFMA of step u (two fragment sets), so they overlap
+        // that step's other MFMAs
+        auto compute = [&](const uint4 *__restrict__ xb, const uint4 *__restrict__ wb) {
+            uint4 xa[2][TM], wf[2][TN];
+            auto read = [&](int u, uint4 (&xr)[TM], uint4 (&wr)[TN]) {
+                const int c = (2 * u + kh) ^ fswz;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) xr[i] = xb[(wm * WM + 32 * i + frag_row) * 8 + c];
+#pragma unroll
+                for (int q = 0; q < TN; ++q) wr[q] = wb[(wn * WN + 32 * q + frag_row) * 8 + c];
+            };
+            auto mma = [&](int u, int i, int q) {
+                acc[i][q] = F16 ? __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                      __builtin_bit_cast(v8h, wf[u & 1][q]),
+                                      __builtin_bit_cast(v8h, xa[u & 1][i]), acc[i][q], 0, 0, 0)
+                                : __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                      __builtin_bit_cast(v8bf, wf[u & 1][q]),
+                                      __builtin_bit_cast(v8bf, xa[u & 1][i]), acc[i][q], 0, 0, 0);
+            };
+            read(0, xa[0], wf[0]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                __builtin_amdgcn_sched_barrier(0);
+                mma(u, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (u < 3) read(u + 1, xa[(u + 1) & 1], wf[(u + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int q = 0; q < TN; ++q)
+                        if (i + q > 0) mma(u, i, q);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // activations of stages 0..2 in flight; at each barrier the stage to
+        // be read next has landed (this wavefront's loads) and been
+        // dequantized (the other role's stores). The buffers a step touches
+        // are distinct, and the restrict qualifiers say so (after inlining the
+        // accesses carry alias scopes, so the fragment reads need not wait for
+        // the direct-to-LDS loads landing in another buffer).
+        load_x(0, xbuf(0));
         __builtin_amdgcn_sched_barrier(0);
-        load_codes(min(s + 3, last), into);
+        load_x(min(1, last), xbuf(1));
         __builtin_amdgcn_sched_barrier(0);
-        // Stage s+1, whose codes compute() dequantizes, has landed once at most
-        // the loads of stages s+2 and s+3 are outstanding. Said explicitly:
-        // the compiler's own wait analysis loses count of one code set across
-        // the unrolled loop and would otherwise drain every load in flight.
-        W4A16_WAIT_VM(2 * NLD);
-        __builtin_amdgcn_sched_barrier(0);  // no use of a loaded value moves above the wait
-        compute(xcur, wcur, deq, wnext);
-        w8a8::vm_barrier<2 * NLD>();
-    };
-#define W4A16_ITER(S, INTO, DEQ) \
-    iteration(S, INTO, DEQ, xbuf((S) + 3), xbuf(S), wbuf(S), wbuf((S) + 1))
-    int s = 0;
-    for (; s + 3 <= nk; s += 3) {
-        W4A16_ITER(s, c0, c1);
-        W4A16_ITER(s + 1, c1, c2);
-        W4A16_ITER(s + 2, c2, c0);
+        load_x(min(2, last), xbuf(2));
+        __builtin_amdgcn_sched_barrier(0);
+        w8a8::vm_barrier<2 * XLD>();
+        auto step = [&](int s, uint4 *__restrict__ xnew, const uint4 *__restrict__ xcur,
+                        const uint4 *__restrict__ wcur) {
+            load_x(min(s + 3, last), xnew);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(xcur, wcur);
+            w8a8::vm_barrier<2 * XLD>();
+        };
+        int s = 0;
+        for (; s + 4 <= nk; s += 4) {
+            step(s, xbuf(s + 3), xbuf(s), wbuf(s));
+            step(s + 1, xbuf(s + 4), xbuf(s + 1), wbuf(s + 1));
+            step(s + 2, xbuf(s + 5), xbuf(s + 2), wbuf(s + 2));
+            step(s + 3, xbuf(s + 6), xbuf(s + 3), wbuf(s + 3));
+        }
+        for (; s < nk; ++s) step(s, xbuf(s + 3), xbuf(s), wbuf(s));
+    } else {
+        // weight codes: thread ct dequantizes columns [CODES * part, +CODES)
+        // of tile row wr
+        constexpr int PARTS = 64 / CODES;
+        const int wr = ct / PARTS, part = ct % PARTS;
+        const int64_t wn_row = min(n0 + wr, N - 1);
+        const uint8_t *wsrc = wq4 + wn_row * (K / 2) + part * (CODES / 2);
+        const uint16_t *ssrc = scales + wn_row * (K / G), *zsrc = zeros + wn_row * (K / G);
+        struct Codes {
+            uint32_t c[CODES / 8];
+            uint16_t s, z;
+        };
+        auto load_codes = [&](int j, Codes &c) {
+            const uint8_t *src = wsrc + 32 * j;
+            if constexpr (CODES == 32) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(src);
+                c.c[0] = v.x; c.c[1] = v.y; c.c[2] = v.z; c.c[3] = v.w;
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2 *>(src);
+                c.c[0] = v.x; c.c[1] = v.y;
+            }
+            const int g = (64 * j + part * CODES) / G;
+            c.s = ssrc[g];
+            c.z = zsrc[g];
+        };
+        auto dequant_into = [&](const Codes &c, uint4 *__restrict__ wb) {
+            const float sf = h_to_float<F16>(c.s), zf = h_to_float<F16>(c.z);
+#pragma unroll
+            for (int i = 0; i < CODES / 8; ++i)
+                wb[wr * 8 + ((part * (CODES / 8) + i) ^ swz(wr))] = dequant8<S4, F16>(c.c[i], sf, zf);
+        };
+        // codes of stages 0..2 in flight, stage 0 dequantized; iteration s
+        // loads stage s + 3 into the set that held stage s (dequantized an
+        // iteration earlier) and dequantizes stage s + 1 into the weight
+        // buffer last read two stages earlier. Stage j's codes live in set
+        // j % 3; unrolling by 3 keeps that rotation free of register copies (a
+        // copy would wait for the load).
+        Codes c0, c1, c2;
+        load_codes(0, c0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(min(1, last), c1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(min(2, last), c2);
+        __builtin_amdgcn_sched_barrier(0);
+        W4A16_WAIT_VM(2 * NC);
+        __builtin_amdgcn_sched_barrier(0);
+        dequant_into(c0, wbuf(0));
+        w8a8::vm_barrier<2 * NC>();
+        auto step = [&](int s, Codes &into, const Codes &deq, uint4 *__restrict__ wnext) {
+            load_codes(min(s + 3, last), into);
+            __builtin_amdgcn_sched_barrier(0);
+            // stage s + 1 has landed once at most the loads of stages s + 2
+            // and s + 3 are outstanding; no use of it moves above the wait
+            W4A16_WAIT_VM(2 * NC);
+            __builtin_amdgcn_sched_barrier(0);
+            dequant_into(deq, wnext);
+            w8a8::vm_barrier<2 * NC>();
+        };
+        int s = 0;
+        for (; s + 3 <= nk; s += 3) {
+            step(s, c0, c1, wbuf(s + 1));
+            step(s + 1, c1, c2, wbuf(s + 2));
+            step(s + 2, c2, c0, wbuf(s + 3));
+        }
+        if (s < nk) { step(s, c0, c1, wbuf(s + 1)); ++s; }
+        if (s < nk) { step(s, c1, c2, wbuf(s + 1)); ++s; }
     }
-    if (s < nk) { W4A16_ITER(s, c0, c1); ++s; }
-    if (s < nk) { W4A16_ITER(s, c1, c2); ++s; }
-#undef W4A16_ITER
     // no load may still be landing in LDS when the epilogue reuses it
     w8a8::vm_barrier<0>();
 
-    // epilogue: tile (i, j), element r of a lane: activation row i*32 + lane%32
-    // of the wavefront's sub-tile, channel j*32 + 8*(r/4) + 4*kh + r%4; the
-    // wavefront's WM x WN bf16 sub-tile is staged in LDS (16-byte chunks of a
-    // row permuted by the row), then stored as whole 16-byte row pieces
+    // epilogue (the multiplying wavefronts): tile (i, j), element r of a lane:
+    // activation row i*32 + lane%32 of the wavefront's sub-tile, channel
+    // j*32 + 8*(r/4) + 4*kh + r%4; the wavefront's WM x WN bf16 sub-tile is
+    // staged in LDS (16-byte chunks of a row permuted by the row), then stored
+    // as whole 16-byte row pieces
     constexpr int CH = WN / 8, PM = CH < 8 ? CH - 1 : 7;
-    uint2 *st8 = reinterpret_cast<uint2 *>(lds) + wave * (WM * WN / 4);
-    const int mw0 = m0 + wm * WM, nw0 = n0 + wn * WN;
+    uint2 *st8 = reinterpret_cast<uint2 *>(lds) + mwave * (WM * WN / 4);
+    const int frag_row = lane & 31, kh = lane >> 5;
+    if (math) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int ml = i * 32 + frag_row;
-                const v16f &a = acc[i][j];
-                const uint32_t lo = pack_h2<F16>(a[4 * g], a[4 * g + 1]);
-                const uint32_t hi = pack_h2<F16>(a[4 * g + 2], a[4 * g + 3]);
-                st8[(ml * CH + ((j * 4 + g) ^ (ml & PM))) * 2 + kh] = make_uint2(lo, hi);
-            }
+                for (int g = 0; g < 4; ++g) {
+                    const int ml = i * 32 + frag_row;
+                    const v16f &a = acc[i][j];
+                    const uint32_t lo = pack_h2<F16>(a[4 * g], a[4 * g + 1]);
+                    const uint32_t hi = pack_h2<F16>(a[4 * g + 2], a[4 * g + 3]);
+                    st8[(ml * CH + ((j * 4 + g) ^ (ml & PM))) * 2 + kh] = make_uint2(lo, hi);
+                }
+    }
     __syncthreads();
+    if (!math) return;
+    const int mw0 = m0 + wm * WM, nw0 = n0 + wn * WN;
     const uint4 *st16 = reinterpret_cast<const uint4 *>(st8);
 #pragma unroll
     for (int it = 0; it < WM * CH / kWave; ++it) {
@@ -570,7 +593,8 @@ hipError_t launch_tiled(const uint16_t *x, int M, const uint8_t *wq4, const uint
                         const uint16_t *zeros, int N, int K, int G, uint16_t *out,
                         hipStream_t stream) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    w4a16_tiled_kernel<BM, BN, WAVES_M, S4, F16><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream>>>(
+    w4a16_tiled_kernel<BM, BN, WAVES_M, S4, F16>
+        <<<dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream>>>(
         x, wq4, scales, zeros, out, M, N, K, G, tiles_m, tiles_n);
     return hipGetLastError();
 }
@@ -601,13 +625,20 @@ hipError_t launch_gemm_codes(const uint16_t *x, int M, const uint8_t *wq4, const
         case 4: return launch_decode_mt<4, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
         default: break;
     }
-    // 256 x 64 tiles (4 wavefronts along M: half the dequantization per output
-    // of 128 x 128, measured faster at M = 1024) when they fill the chip, then
-    // 128 x 64 (also 4 wavefronts along M), else 64 x 64
-    const long t256 = (long)((M + 255) / 256) * ((N + 63) / 64);
-    const long t128 = (long)((M + 127) / 128) * ((N + 63) / 64);
-    if (t256 >= 256) return launch_tiled<256, 64, 4, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
-    if (t128 >= 256) return launch_tiled<128, 64, 4, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    // The largest tile that still gives every CU a workgroup: a tile's time is
+    // set by its K loop (its activation stream and stage barriers), so larger
+    // tiles share it over more outputs but leave CUs idle below 256 tiles
+    // (N = K = 4096: M = 2048 256 x 128, 80 us; M = 1024 256 x 64, 50 us;
+    // M = 512 128 x 64, 32 us; M = 128 and 256 64 x 64, 26-27 us). Taller
+    // tiles first: a column more costs every row tile a dequantization.
+    auto tiles = [&](long bm, long bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    const long fill = w8a8::device_cu_count();
+    if (tiles(256, 128) >= fill)
+        return launch_tiled<256, 128, 2, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    if (tiles(256, 64) >= fill)
+        return launch_tiled<256, 64, 4, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
+    if (tiles(128, 64) >= fill)
+        return launch_tiled<128, 64, 4, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
     return launch_tiled<64, 64, 2, S4, F16>(x, M, wq4, scales, zeros, N, K, G, out, stream);
 }
 

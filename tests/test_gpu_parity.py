@@ -649,10 +649,12 @@ def _w4a16_case(b, oracle, inp, what, rows=None, signed=False):
     (1, 16, 128, 128), (5, 48, 256, 32), (16, 128, 4096, 128), (17, 64, 640, 64),
     (33, 32, 1024, 256), (64, 96, 512, 128), (1, 32, 4096, 128), (9, 64, 8192, 256),
     (5, 48, 4224, 128), (16, 32, 6144, 64),
-    # tiled path: 64 x 64 tiles (ragged M and N), 128 x 64 and 256 x 64 tiles (256+ of them)
+    # tiled path: 64 x 64 tiles (ragged M and N), 128 x 64, 256 x 64 and 256 x 128 tiles
+    # (256+ of them)
     (65, 64, 128, 128), (100, 80, 384, 32), (130, 272, 1024, 64), (257, 528, 256, 128),
     (400, 4160, 256, 64), (300, 8192, 128, 32),
     (2048, 2048, 256, 128), (1100, 4096, 128, 128), (1024, 4112, 256, 64), (512, 8192, 384, 128),
+    (2050, 4112, 128, 32),
 ])
 def test_w4a16_gemm_shapes(b, oracle, M, N, K, G):
     log(f"w4a16 gemm M={M} N={N} K={K} G={G}")
