@@ -169,6 +169,18 @@ def prepare(name: str, torch, np, b, dev):
     return d
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first `model name` line of /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(name: str, np):
     """The CPU oracle (untuned) on a bounded sample of the same workload."""
     import oracle
@@ -200,7 +212,7 @@ def cpu_baseline(name: str, np):
     if sparse24 is not None:
         ops /= 2          # the kept products only, as the GPU line counts them
     return {"value": round(ops / t / 1e12, 6), "unit": "TOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"rows 0..{rows - 1} of the {name} workload (M={M}, N={N}, K={K}): "
                       f"quantize + exact int GEMM + float64 epilogue"
                       + (" (2:4 weight decompressed inside the timed region)" if sparse24 else "")
