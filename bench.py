@@ -29,7 +29,11 @@ The line also carries:
                (the M=16 weight matrix) with the buffers rotated past the
                Infinity Cache, grid-stride and in the M-small GEMM's own
                row-slice pattern (decode_m16.vs_measured_read_floor takes the
-               faster of the two). roofline.frac_measured is the kernel's rate
+               faster of the two), and the prefill GEMM's operand stream alone
+               (its tiles, tile order, direct-to-LDS ring and barriers, no
+               arithmetic) over operand sets rotated past the Infinity Cache
+               (roofline.operand_stream_us and frac_of_operand_stream on the
+               prefill line). roofline.frac_measured is the kernel's rate
                against these (for HBM-bound kernels: the time its read and
                write bytes take at the measured rates, over its time);
   clocks       amd-smi's gfx and memory clocks sampled while the step's HIP
@@ -234,7 +238,9 @@ def measure_peaks(torch, eager=False):
     lib.peaks_read.argtypes = [p, i64, i32, p, p]
     lib.peaks_write.argtypes = [p, i64, i32, p]
     lib.peaks_read_rows.argtypes = [p, i32, p, p]
-    for f in (lib.peaks_mfma_i8, lib.peaks_read, lib.peaks_write, lib.peaks_read_rows):
+    lib.peaks_operand_stream.argtypes = [p, p, i32, i32, i32, p, p]
+    for f in (lib.peaks_mfma_i8, lib.peaks_read, lib.peaks_write, lib.peaks_read_rows,
+              lib.peaks_operand_stream):
         f.restype = i32
     dev = torch.device("cuda:0")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -275,6 +281,20 @@ def measure_peaks(torch, eager=False):
     # every load in flight at once): the floor that kernel is rated against
     rr = lambda i: call(lib.peaks_read_rows(bufs[i % R].data_ptr(), 4096, sink.data_ptr(), stream()))
     read_rows_us = time_median(rr, 20 * R, torch, R, eager) * 1e3
+    del bufs
+    # the prefill GEMM's operand stream alone (M = 2048, N = K = 4096), operand sets rotated
+    Mp, Np, Kp = 2048, 4096, 4096
+    Ro = rotation((Mp + Np) * Kp)
+    ops = [(torch.empty(Mp * Kp, dtype=torch.uint8, device=dev),
+            torch.empty(Np * Kp, dtype=torch.uint8, device=dev)) for _ in range(Ro)]
+    for a, bb in ops:
+        call(lib.peaks_write(a.data_ptr(), Mp * Kp, 8 * cus, stream()))
+        call(lib.peaks_write(bb.data_ptr(), Np * Kp, 8 * cus, stream()))
+    osink = torch.zeros((Mp // 256) * (Np // 128) * 256, dtype=torch.int32, device=dev)
+    os_ = lambda i: call(lib.peaks_operand_stream(ops[i % Ro][0].data_ptr(), ops[i % Ro][1].data_ptr(),
+                                                  Mp, Np, Kp, osink.data_ptr(), stream()))
+    operand_us = time_median(os_, 10 * Ro, torch, Ro, eager) * 1e3
+    del ops
     torch.cuda.synchronize()
     return {"mfma_int8_TOPs": round(mfma_tops, 1), "mfma_loop_shader_MHz": round(shader_mhz, 1),
             "hbm_read_GBps": round(read_gbs, 1), "hbm_write_GBps": round(write_gbs, 1),
@@ -282,11 +302,15 @@ def measure_peaks(torch, eager=False):
             "read_16_8MB_GBps": round(small / (read_small_us * 1e-6) / 1e9, 1),
             "read_16_8MB_rows_us": round(read_rows_us, 3),
             "read_16_8MB_rows_GBps": round(small / (read_rows_us * 1e-6) / 1e9, 1),
+            "prefill_operand_stream_us": round(operand_us, 3),
+            "prefill_operand_stream_GBps_per_CU": round((256 + 128) * Kp / (operand_us * 1e-6) / 1e9, 1),
             "method": "libpeaks.so: 8 independent v_mfma_i32_32x32x32_i8 chains per wavefront, "
                       f"{wgs} workgroups of 4 wavefronts; 16-byte loads / streaming stores over "
                       "1 GiB; 16.8 MB reads over rotated buffers, grid-stride and in the M-small "
                       "GEMM's row-slice pattern (256 workgroups, 16 loads per lane in flight); "
-                      "HIP graph replays, median of 5"}
+                      "the 2048 x 4096 x 4096 GEMM's operand stream alone (256 x 128 tiles in its "
+                      "tile order, 3-stage direct-to-LDS ring, its waits and barriers, no arithmetic) "
+                      f"over {Ro} rotated operand sets; HIP graph replays, median of 5"}
 
 
 def amd_smi_clocks():
@@ -666,6 +690,9 @@ def main():
         clocks = clocks_under_load(step, torch, R)
     if roof["bound"] == "mfma" and name == "prefill_outliers":
         roof["mfma_counters"] = mfma_record()
+        if peaks:
+            roof["operand_stream_us"] = peaks["prefill_operand_stream_us"]
+            roof["frac_of_operand_stream"] = round(peaks["prefill_operand_stream_us"] / (ms_gemm * 1e3), 4)
     kernel = "w8a8_bsr_gemm" if bsr else "w8a8_sparse24_gemm" if sp24 else "w8a8_gemm"
     roof["kernel"] = kernel
     roof["avg_launch_us"] = round(ms_gemm * 1e3, 3)

@@ -14,6 +14,10 @@
 //   dropped).
 // peaks_write: every thread writes 16-byte chunks, grid-stride, with streaming
 //   stores (as the GEMM epilogues do).
+// peaks_operand_stream: the large-M GEMM's operand stream alone (256 x 128
+//   tiles in its tile order, 128-byte K stages through a 3-stage direct-to-LDS
+//   ring with its counted waits and one barrier per stage; no fragment reads,
+//   MFMAs or epilogue): the time that kernel's loads take by themselves.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -80,6 +84,67 @@ __global__ __launch_bounds__(256) void read_rows(const int8_t *__restrict__ p, u
     if (s == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+
+// Wait until at most N vector-memory operations are outstanding, then meet the
+// workgroup at a barrier.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// A [M, K] and B [N, K] int8 (M % 256 == 0, N % 128 == 0, K % 128 == 0),
+// one workgroup of 4 wavefronts per 256 x 128 tile. Tile order: each XCD
+// (workgroup i runs on XCD i % 8) owns a contiguous range of tiles, taken in
+// groups of 4 tile rows. A stage is 384 rows x 128 bytes: load l of wavefront
+// w fills 16-byte slots 64 (w + 4 l) .. of the stage, 8 rows x 128 bytes
+// (chunk c of row r lands at slot 8 r + (c ^ (r % 8) ^ ((r / 8) % 2))). Stage
+// s + 2 is issued before stage s + 1 is awaited.
+__global__ __launch_bounds__(256, 1) void operand_stream(const int8_t *__restrict__ A,
+                                                         const int8_t *__restrict__ B, int K,
+                                                         int tiles_m, int tiles_n, uint32_t *sink) {
+    constexpr int BM = 256, BN = 128, STAGE = (BM + BN) * 8, A_LD = BM / 32, NLD = (BM + BN) / 32;
+    __shared__ uint4 lds[3 * STAGE];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tiles = tiles_m * tiles_n;
+    const int q = tiles / 8, r = tiles % 8, xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+    const int t = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+    const int per_group = 4 * tiles_n, first_m = (t / per_group) * 4;
+    const int gsize = min(tiles_m - first_m, 4);
+    const int m0 = (first_m + (t % per_group) % gsize) * BM, n0 = ((t % per_group) / gsize) * BN;
+    const int row = 8 * wave + (lane >> 3);  // + 32 l
+    const int kc = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);
+    const int8_t *src[NLD];
+#pragma unroll
+    for (int l = 0; l < NLD; ++l)
+        src[l] = l < A_LD ? A + (int64_t)(m0 + row + 32 * l) * K + 16 * kc
+                          : B + (int64_t)(n0 + row + 32 * (l - A_LD)) * K + 16 * kc;
+    const int nk = K / 128;
+    auto issue = [&](int s) {
+        uint4 *dst = lds + (s % 3) * STAGE;
+        const int k0 = 128 * min(s, nk - 1);  // stages past the last reload the last
+#pragma unroll
+        for (int l = 0; l < NLD; ++l)
+            __builtin_amdgcn_global_load_lds((global_void *)(src[l] + k0), (lds_void *)(dst + 64 * (wave + 4 * l)),
+                                             16, 0, 0);
+    };
+    issue(0);
+    issue(1);
+    vm_barrier<NLD>();
+    for (int s = 0; s < nk; ++s) {
+        issue(s + 2);
+        vm_barrier<NLD>();
+    }
+    vm_barrier<0>();
+    const uint32_t v = reinterpret_cast<const uint32_t *>(lds)[threadIdx.x];
+    if (v == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + threadIdx.x] = v;
+}
+
 __global__ __launch_bounds__(256) void write_loop(uint4 *__restrict__ p, int64_t n16, uint32_t v) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
@@ -116,6 +181,16 @@ int peaks_read_rows(const void *buf, int rows, uint32_t *sink, void *stream) {
     if (rows <= 0 || rows % 16 || !buf || !sink) return -1;
     read_rows<<<rows / 16, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const int8_t *>(buf),
                                                                          sink);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+// a: [M, K], b: [N, K] int8; M a positive multiple of 256, N of 128, K of 128;
+// sink: at least (M / 256) * (N / 128) * 256 words.
+int peaks_operand_stream(const void *a, const void *b, int M, int N, int K, uint32_t *sink, void *stream) {
+    if (!a || !b || !sink || M <= 0 || N <= 0 || K <= 0 || M % 256 || N % 128 || K % 128) return -1;
+    const int tm = M / 256, tn = N / 128;
+    operand_stream<<<tm * tn, 256, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const int8_t *>(a), static_cast<const int8_t *>(b), K, tm, tn, sink);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
