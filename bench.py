@@ -33,7 +33,8 @@ The line also carries:
                (its tiles, tile order, direct-to-LDS ring and barriers, no
                arithmetic) over operand sets rotated past the Infinity Cache
                (roofline.operand_stream_us and frac_of_operand_stream on the
-               prefill line). roofline.frac_measured is the kernel's rate
+               prefill line), and over one set that stays in the cache.
+               roofline.frac_measured is the kernel's rate
                against these (for HBM-bound kernels: the time its read and
                write bytes take at the measured rates, over its time);
   clocks       amd-smi's gfx and memory clocks sampled while the step's HIP
@@ -294,6 +295,11 @@ def measure_peaks(torch, eager=False):
     os_ = lambda i: call(lib.peaks_operand_stream(ops[i % Ro][0].data_ptr(), ops[i % Ro][1].data_ptr(),
                                                   Mp, Np, Kp, osink.data_ptr(), stream()))
     operand_us = time_median(os_, 10 * Ro, torch, Ro, eager) * 1e3
+    # the same stream over one operand set, which then stays in the Infinity Cache: the
+    # difference is the cost of filling the L2s from HBM
+    oc = lambda i: call(lib.peaks_operand_stream(ops[0][0].data_ptr(), ops[0][1].data_ptr(),
+                                                 Mp, Np, Kp, osink.data_ptr(), stream()))
+    operand_cached_us = time_median(oc, 10 * Ro, torch, 1, eager) * 1e3
     del ops
     torch.cuda.synchronize()
     return {"mfma_int8_TOPs": round(mfma_tops, 1), "mfma_loop_shader_MHz": round(shader_mhz, 1),
@@ -304,13 +310,15 @@ def measure_peaks(torch, eager=False):
             "read_16_8MB_rows_GBps": round(small / (read_rows_us * 1e-6) / 1e9, 1),
             "prefill_operand_stream_us": round(operand_us, 3),
             "prefill_operand_stream_GBps_per_CU": round((256 + 128) * Kp / (operand_us * 1e-6) / 1e9, 1),
+            "prefill_operand_stream_cached_us": round(operand_cached_us, 3),
             "method": "libpeaks.so: 8 independent v_mfma_i32_32x32x32_i8 chains per wavefront, "
                       f"{wgs} workgroups of 4 wavefronts; 16-byte loads / streaming stores over "
                       "1 GiB; 16.8 MB reads over rotated buffers, grid-stride and in the M-small "
                       "GEMM's row-slice pattern (256 workgroups, 16 loads per lane in flight); "
                       "the 2048 x 4096 x 4096 GEMM's operand stream alone (256 x 128 tiles in its "
                       "tile order, 3-stage direct-to-LDS ring, its waits and barriers, no arithmetic) "
-                      f"over {Ro} rotated operand sets; HIP graph replays, median of 5"}
+                      f"over {Ro} rotated operand sets, and over one set (Infinity Cache resident); "
+                      "HIP graph replays, median of 5"}
 
 
 def amd_smi_clocks():
