@@ -12,7 +12,10 @@ The line also carries:
                ops per launch / average launch time, against the int8 dense
                MFMA peak; traffic from the committed rocprofv3 PMC record when
                it was taken on the current kernel source, else null;
-  cpu_baseline the CPU oracle timed on this host on a bounded sample;
+  cpu_baseline the CPU oracle timed on this host on a bounded sample (threads,
+               CPU model), and its `parity`: the oracle's rows of that sample
+               against the timed path's output for the same inputs (Xq and sx
+               bit for bit, bf16 ulps);
   library_int_mm  the vendor library's int8 GEMM (torch._int_mm, hipBLASLt,
                int32 out, no dequant) on the same inputs, for dense M > 16;
   decode_m16   the M=16 weight-streaming path (K=N=4096): GB/s of the GEMM
@@ -186,8 +189,19 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(name: str, np):
-    """The CPU oracle (untuned) on a bounded sample of the same workload."""
+def bf16_ulps(a, b, np):
+    """Distance in bf16 ulps between two arrays of bf16 bit patterns (sign-magnitude mapped
+    to ordered integers; +0 and -0 coincide)."""
+    def ordered(u):
+        u = u.astype(np.int32) & 0xFFFF
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(ordered(a) - ordered(b))
+
+
+def cpu_baseline(name: str, np, gpu_rows=None):
+    """The CPU oracle (untuned) on a bounded sample of the same workload. gpu_rows(r), when
+    given, returns the timed path's Xq, sx and bf16 output bits for rows 0..r-1 of the same
+    inputs: the oracle's rows are then compared with them (the `parity` entry)."""
     import oracle
     from quantized_gemm_quantize_amd.inputs import bsr_from_dense, make_inputs
     inp = make_inputs(name, seed=0)
@@ -206,22 +220,30 @@ def cpu_baseline(name: str, np):
             acc = oracle.gemm_i32(xq, wq)
         else:
             acc = oracle.bsr_gemm_i32(xq, *bsr, N)
-        oracle.epilogue_bf16(acc, sx, sw)
-        return time.perf_counter() - t0
+        out = oracle.epilogue_bf16(acc, sx, sw)
+        return time.perf_counter() - t0, xq, sx, out
 
     probe = min(M, 64)
-    t_probe = run(probe)
+    t_probe = run(probe)[0]
     rows = int(min(M, max(probe, probe * 15.0 / max(t_probe, 1e-6))))
-    t = run(rows)
+    t, xq, sx, out = run(rows)
     ops = 2.0 * rows * N * K
     if sparse24 is not None:
         ops /= 2          # the kept products only, as the GPU line counts them
+    parity = None
+    if gpu_rows is not None:
+        g_xq, g_sx, g_out = gpu_rows(rows)
+        ulps = bf16_ulps(g_out, out, np)
+        parity = {"rows": rows, "xq_bit_exact": bool(np.array_equal(g_xq, xq)),
+                  "sx_bit_exact": bool(np.array_equal(g_sx.view(np.uint32), sx.view(np.uint32))),
+                  "max_ulp": int(ulps.max()), "frac_beyond_1ulp": float((ulps > 1).mean()),
+                  "bar": "Xq and sx bit-exact, bf16 within 1 ulp"}
     return {"value": round(ops / t / 1e12, 6), "unit": "TOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"rows 0..{rows - 1} of the {name} workload (M={M}, N={N}, K={K}): "
                       f"quantize + exact int GEMM + float64 epilogue"
                       + (" (2:4 weight decompressed inside the timed region)" if sparse24 else "")
-                      + f", {t:.2f} s wall"}
+                      + f", {t:.2f} s wall", "parity": parity}
 
 
 MFMA_RECORD = os.path.join(ROOT, "profiles", "gemm_tiled_prefill_mfma.json")
@@ -429,8 +451,10 @@ def bench_decode(torch, np, b, dev, steps, warmup, eager=False):
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 
 
-def w4a16_cpu_baseline(inp, np):
-    """The CPU oracle (dequantization + float64-summed bf16 GEMM) on a bounded row sample."""
+def w4a16_cpu_baseline(inp, np, gpu_rows=None):
+    """The CPU oracle (dequantization + float64-summed bf16 GEMM) on a bounded row sample;
+    with gpu_rows(r) (the timed kernel's bf16 output bits for rows 0..r-1 of the same inputs)
+    the oracle's rows are compared with them (the `parity` entry)."""
     import oracle
     M, K = inp.x_bits.shape
     N = inp.wq4.shape[0]
@@ -438,18 +462,25 @@ def w4a16_cpu_baseline(inp, np):
     def run(rows):
         t0 = time.perf_counter()
         w = oracle.w4a16_dequant(inp.wq4, inp.scales, inp.zeros)
-        oracle.bf16_gemm(inp.x_bits[:rows], w)
-        return time.perf_counter() - t0
+        out = oracle.bf16_gemm(inp.x_bits[:rows], w)
+        return time.perf_counter() - t0, out
 
     probe = min(M, 8)
-    t_probe = run(probe)
+    t_probe = run(probe)[0]
     rows = int(min(M, max(probe, probe * 15.0 / max(t_probe, 1e-6))))
-    t = run(rows)
+    t, out = run(rows)
+    parity = None
+    if gpu_rows is not None:
+        ulps = bf16_ulps(gpu_rows(rows), out, np)
+        parity = {"rows": rows, "max_ulp": int(ulps.max()),
+                  "frac_beyond_1ulp": float((ulps > 1).mean()),
+                  "bar": "the fp32 summation bound of the tests (at most 1e-3 of the outputs "
+                         "beyond 1 ulp)"}
     return {"value": round(2.0 * rows * N * K / t / 1e12, 6), "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"rows 0..{rows - 1} of the W4A16 layer (M={M}, N={N}, K={K}): "
                       f"dequantization of the whole weight + float64-summed bf16 GEMM, "
-                      f"{t:.2f} s wall"}
+                      f"{t:.2f} s wall", "parity": parity}
 
 
 def bench_w4a16(args, torch, np, b, dev):
@@ -528,7 +559,10 @@ def bench_w4a16(args, torch, np, b, dev):
         "sweep_n4096_k4096_g128": sweep,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = w4a16_cpu_baseline(inp, np)
+        out0 = b.w4a16_gemm(x, *ws[0])
+        torch.cuda.synchronize()
+        gpu_rows = lambda r: out0[:r].view(torch.int16).cpu().numpy().view(np.uint16)
+        line["cpu_baseline"] = w4a16_cpu_baseline(inp, np, gpu_rows)
     print(json.dumps(line), flush=True)
 
 
@@ -609,6 +643,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
     eager_out = outs[0].clone()
+    eager_xq, eager_sx = xqs[0].clone(), sxs[0].clone()
     ms_step = time_loop(step, args.steps, torch, period=R, eager=args.eager)
     # graph replays recompute the same outputs: check the first set bit for bit
     if not torch.equal(outs[0].view(torch.int16), eager_out.view(torch.int16)):
@@ -750,7 +785,9 @@ def main():
         line["peaks"] = peaks
         line["clocks"] = clocks
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(name, np)
+        gpu_rows = lambda r: (eager_xq[:r].cpu().numpy(), eager_sx[:r].cpu().numpy(),
+                              eager_out[:r].view(torch.int16).cpu().numpy().view(np.uint16))
+        line["cpu_baseline"] = cpu_baseline(name, np, gpu_rows)
     print(json.dumps(line), flush=True)
 
 
