@@ -26,7 +26,8 @@ The line also carries:
 
   peaks        reference rates measured on the same GPU in the same run
                (libpeaks.so): the int8 MFMA issue rate of back-to-back
-               v_mfma_i32_32x32x32_i8 with the shader clock it ran at
+               v_mfma_i32_32x32x32_i8 (and the bf16 rate of
+               v_mfma_f32_32x32x16_bf16) with the shader clock it ran at
                (s_memtime against the 100 MHz reference), HBM streaming read
                and write rates over 1 GiB, and the time to stream-read 16.8 MB
                (the M=16 weight matrix) with the buffers rotated past the
@@ -258,12 +259,13 @@ def measure_peaks(torch, eager=False):
     lib = ctypes.CDLL(PEAKS_LIB)
     p, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.peaks_mfma_i8.argtypes = [i32, i32, p, p, p]
+    lib.peaks_mfma_bf16.argtypes = [i32, i32, p, p, p]
     lib.peaks_read.argtypes = [p, i64, i32, p, p]
     lib.peaks_write.argtypes = [p, i64, i32, p]
     lib.peaks_read_rows.argtypes = [p, i32, p, p]
     lib.peaks_operand_stream.argtypes = [p, p, i32, i32, i32, p, p]
-    for f in (lib.peaks_mfma_i8, lib.peaks_read, lib.peaks_write, lib.peaks_read_rows,
-              lib.peaks_operand_stream):
+    for f in (lib.peaks_mfma_i8, lib.peaks_mfma_bf16, lib.peaks_read, lib.peaks_write,
+              lib.peaks_read_rows, lib.peaks_operand_stream):
         f.restype = i32
     dev = torch.device("cuda:0")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -282,6 +284,12 @@ def measure_peaks(torch, eager=False):
     c = clk.cpu().tolist()
     mfma_tops = wgs * 4 * iters * 8 * 65536 / (ms * 1e-3) / 1e12
     shader_mhz = c[0] / (c[1] / 100e6) / 1e6 if c[1] else None
+    mb = lambda i: call(lib.peaks_mfma_bf16(wgs, iters, sink.data_ptr(), clk.data_ptr(), stream()))
+    mb(0)
+    ms_bf16 = time_median(mb, 20, torch, 1, eager)
+    cb = clk.cpu().tolist()
+    bf16_tflops = wgs * 4 * iters * 8 * 32768 / (ms_bf16 * 1e-3) / 1e12
+    bf16_mhz = cb[0] / (cb[1] / 100e6) / 1e6 if cb[1] else None
 
     nbytes = 1 << 30
     big = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -325,6 +333,7 @@ def measure_peaks(torch, eager=False):
     del ops
     torch.cuda.synchronize()
     return {"mfma_int8_TOPs": round(mfma_tops, 1), "mfma_loop_shader_MHz": round(shader_mhz, 1),
+            "mfma_bf16_TFLOPs": round(bf16_tflops, 1), "mfma_bf16_loop_shader_MHz": round(bf16_mhz, 1),
             "hbm_read_GBps": round(read_gbs, 1), "hbm_write_GBps": round(write_gbs, 1),
             "read_16_8MB_us": round(read_small_us, 3),
             "read_16_8MB_GBps": round(small / (read_small_us * 1e-6) / 1e9, 1),
@@ -333,7 +342,8 @@ def measure_peaks(torch, eager=False):
             "prefill_operand_stream_us": round(operand_us, 3),
             "prefill_operand_stream_GBps_per_CU": round((256 + 128) * Kp / (operand_us * 1e-6) / 1e9, 1),
             "prefill_operand_stream_cached_us": round(operand_cached_us, 3),
-            "method": "libpeaks.so: 8 independent v_mfma_i32_32x32x32_i8 chains per wavefront, "
+            "method": "libpeaks.so: 8 independent v_mfma_i32_32x32x32_i8 (and, separately, "
+                      "v_mfma_f32_32x32x16_bf16) chains per wavefront, "
                       f"{wgs} workgroups of 4 wavefronts; 16-byte loads / streaming stores over "
                       "1 GiB; 16.8 MB reads over rotated buffers, grid-stride and in the M-small "
                       "GEMM's row-slice pattern (256 workgroups, 16 loads per lane in flight); "
@@ -527,6 +537,16 @@ def bench_w4a16(args, torch, np, b, dev):
         roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
     roof.update({"traffic": None, "kernel": "w4a16_gemm", "avg_launch_us": round(ms * 1e3, 3)})
+    peaks = None
+    if not args.no_peaks:
+        peaks = measure_peaks(torch, args.eager)
+        if roof["bound"] == "mfma":
+            roof["frac_measured"] = round(roof["achieved"] / peaks["mfma_bf16_TFLOPs"], 4)
+            roof["peak_measured"] = peaks["mfma_bf16_TFLOPs"]
+        else:
+            t_ideal = ((2 * M * K + w_bytes) / (peaks["hbm_read_GBps"] * 1e9)
+                       + 2 * M * N / (peaks["hbm_write_GBps"] * 1e9))
+            roof["frac_measured"] = round(t_ideal / (ms * 1e-3), 4)
     # the other code and value formats at the same M (signed codes, binary16 values)
     formats = {}
     for name, sg, hf in (("s4_bf16", True, False), ("u4_f16", False, True), ("s4_f16", True, True)):
@@ -563,6 +583,8 @@ def bench_w4a16(args, torch, np, b, dev):
         torch.cuda.synchronize()
         gpu_rows = lambda r: out0[:r].view(torch.int16).cpu().numpy().view(np.uint16)
         line["cpu_baseline"] = w4a16_cpu_baseline(inp, np, gpu_rows)
+    if peaks is not None:
+        line["peaks"] = peaks
     print(json.dumps(line), flush=True)
 
 

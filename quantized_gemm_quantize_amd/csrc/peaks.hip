@@ -8,6 +8,8 @@
 //   v_mfma_i32_32x32x32_i8 on register operands (8 accumulators, so the issue
 //   never waits on a result); 65536 ops each. The operands are varied per lane
 //   so the multipliers toggle as under real data.
+// peaks_mfma_bf16: the same with v_mfma_f32_32x32x16_bf16 (32768 flops each;
+//   operands are finite bf16 values in [1, 2) whose mantissas vary per lane).
 // peaks_read: every thread reads 16-byte chunks, grid-stride, with the
 //   nontemporal hint (as the kernels that read their weights once do), and
 //   folds them into one word per thread (written once, so the loads cannot be
@@ -47,6 +49,41 @@ __global__ __launch_bounds__(256) void mfma_loop(int iters, int *sink, uint64_t 
 #pragma unroll
         for (int e = 0; e < 16; ++e) s ^= acc[i][e];
     if (s == 0x7fffffff) sink[blockIdx.x] = s;  // practically never: keeps the loop alive
+    const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        clk[0] = c1 - c0;
+        clk[1] = r1 - r0;
+    }
+}
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void mfma_loop_bf16(int iters, int *sink, uint64_t *clk) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    // 8 bf16 per operand: exponent of 1.0 (0x3F80), mantissa bits from the lane
+    v4i a = {0x3F803F80 | (lane * 0x00130017 & 0x007F007F), 0x3F803F80 | (lane * 0x001D0005 & 0x007F007F),
+             0x3F803F80 | ((lane ^ 0x55) * 0x00070003 & 0x007F007F), 0x3F803F80 | (~lane & 0x007F007F)};
+    v4i b = {0x3F803F80 | (lane * 0x000B0029 & 0x007F007F), 0x3F803F80 | ((lane ^ 0x33) & 0x007F007F),
+             0x3F803F80 | (lane * 0x00250011 & 0x007F007F), 0x3F803F80 | (lane * 0x0003001F & 0x007F007F)};
+    v16f acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = v16f{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b),
+                                                             acc[i], 0, 0, 0);
+        const int m = it & 0x007F;
+        a = a ^ (v4i){m, m << 16, m, m << 16};  // mantissa bits only: the operands stay in [1, 2)
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[i][e];
+    if (s == -1.0f) sink[blockIdx.x] = 1;  // never (every product is positive): keeps the loop alive
     const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         clk[0] = c1 - c0;
@@ -164,6 +201,13 @@ extern "C" {
 int peaks_mfma_i8(int workgroups, int iters, int *sink, uint64_t *clk, void *stream) {
     if (workgroups <= 0 || iters <= 0 || !sink || !clk) return -1;
     mfma_loop<<<workgroups, 256, 0, static_cast<hipStream_t>(stream)>>>(iters, sink, clk);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+// As peaks_mfma_i8, with bf16 operands: the flops are workgroups * 4 * iters * 8 * 32768.
+int peaks_mfma_bf16(int workgroups, int iters, int *sink, uint64_t *clk, void *stream) {
+    if (workgroups <= 0 || iters <= 0 || !sink || !clk) return -1;
+    mfma_loop_bf16<<<workgroups, 256, 0, static_cast<hipStream_t>(stream)>>>(iters, sink, clk);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
