@@ -663,9 +663,11 @@ def test_w4a16_gemm_shapes(b, oracle, M, N, K, G):
 
 @pytest.mark.parametrize("M,N,K,G", [(16, 128, 4096, 128), (33, 32, 1024, 256),
                                      (130, 272, 1024, 64), (400, 4160, 256, 64),
-                                     (1024, 4112, 256, 64), (7, 48, 8192, 128)])
+                                     (1024, 4112, 256, 64), (7, 48, 8192, 128),
+                                     (2050, 4112, 128, 32)])
 def test_w4a16_gemm_signed_codes(b, oracle, M, N, K, G):
-    """s4 codes on each kernel path (weight streaming, 64x64, 128x64 and 256x64 tiles)."""
+    """s4 codes on each kernel path (weight streaming, 64x64, 128x64, 256x64 and 256x128
+    tiles)."""
     log(f"w4a16 gemm s4 M={M} N={N} K={K} G={G}")
     _w4a16_case(b, oracle, make_w4a16(M, N, K, G, seed=M + N + K + 1, signed=True),
                 f"s4 M={M} N={N} K={K}", signed=True)
@@ -674,7 +676,7 @@ def test_w4a16_gemm_signed_codes(b, oracle, M, N, K, G):
 @pytest.mark.parametrize("signed", [False, True])
 @pytest.mark.parametrize("M,N,K,G", [(16, 128, 4096, 128), (33, 32, 1024, 256),
                                      (130, 272, 1024, 64), (400, 4160, 256, 64),
-                                     (1024, 4112, 256, 64)])
+                                     (1024, 4112, 256, 64), (2050, 4112, 128, 32)])
 def test_w4a16_gemm_f16(b, oracle, M, N, K, G, signed):
     """IEEE binary16 activations, scales, zeros and outputs on each kernel path."""
     log(f"w4a16 gemm f16 M={M} N={N} K={K} G={G} signed={signed}")
