@@ -14,6 +14,9 @@
 //  - the K-split partial int32 tiles are summed in LDS (never in HBM), then
 //    scaled, rounded to bf16 and stored: the same fused epilogue as the tiled
 //    kernel.
+// For M <= 16 and K >= 3072 (the decode shapes) gemm_decode_lds_kernel below
+// takes over: the same split and epilogue, with both operands moved global ->
+// LDS in whole cache lines. The register kernel serves the rest of M <= 64.
 //
 // The single-launch linear (linear_decode_kernel) is the same kernel with the
 // activation quantization moved into its prologue (pytorch/ao PR #821 asks for
